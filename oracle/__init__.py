@@ -1,0 +1,106 @@
+"""Float64 CPU oracle for relative-bias grouped-query attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the library never does. It shares
+no code with the HIP path (see ``oracle.c`` for the definition it computes and
+the passages of the pages it follows).
+
+``attend`` takes float64 NumPy arrays with contiguous (un-paged) keys and
+values; un-paging a block-table cache is the caller's job (a plain gather).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (float64, OpenMP). Always rebuilds."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                    "-Wall", "-Werror", _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64, dbl, P = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.rba_oracle_attend.argtypes = [i64, P, P, i64, i64, i64, i64, i64, i64, dbl,
+                                          P, P, P, P, P, i64, P, P]
+        lib.rba_oracle_attend.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
+           rows=None, out=None, lse=None):
+    """Relative-bias GQA attention, float64, over contiguous K/V.
+
+    q    [total_q, Hq, dqk]      rows of all sequences packed in order
+    k    [total_kv, Hkv, dqk]    sequence b owns seq_lens[b] consecutive rows
+    v    [total_kv, Hkv, dv]
+    rel  [total_q, Hq, R]
+    q_lens, seq_lens  per-sequence query rows and key count (q_len <= seq_len;
+                      the queries are the last q_len positions)
+    rows  optional iterable of global query rows to compute (others stay NaN)
+    Returns (out [total_q, Hq, dv], lse [total_q, Hq]) as float64.
+    """
+    lib = _load()
+    q, k, v, rel = _f64(q), _f64(k), _f64(v), _f64(rel)
+    q_lens = np.ascontiguousarray(q_lens, dtype=np.int64)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+    total_q, Hq, dqk = q.shape
+    Hkv, dv = k.shape[1], v.shape[2]
+    R = rel.shape[2]
+    if R != rel_extent:
+        raise ValueError("rel last dim must equal rel_extent")
+    if q_lens.sum() != total_q or seq_lens.sum() != k.shape[0] or v.shape[0] != k.shape[0]:
+        raise ValueError("q_lens/seq_lens do not match the packed shapes")
+    if out is None:
+        out = np.full((total_q, Hq, dv), np.nan)
+    if lse is None:
+        lse = np.full((total_q, Hq), np.nan)
+    rows_arr = None
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int64))
+    rc = lib.rba_oracle_attend(
+        len(q_lens), q_lens.ctypes.data, seq_lens.ctypes.data,
+        Hq, Hkv, dqk, dv, int(rel_extent), int(window), float(scale),
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, rel.ctypes.data,
+        rows_arr.ctypes.data if rows_arr is not None else None,
+        len(rows_arr) if rows_arr is not None else 0,
+        out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, lse
+
+
+def unpage(cache, block_tables, seq_lens, block_size=128):
+    """Gather a paged cache [num_blocks, H, block_size, d] into contiguous
+    per-sequence rows [sum(seq_lens), H, d] (sequence b: logical block n is
+    physical block block_tables[b][n], slot s is position n*block_size + s)."""
+    cache = np.asarray(cache)
+    parts = []
+    for b, L in enumerate(seq_lens):
+        nb = (int(L) + block_size - 1) // block_size
+        blocks = cache[np.asarray(block_tables[b][:nb], dtype=np.int64)]  # [nb, H, bs, d]
+        seq = blocks.transpose(0, 2, 1, 3).reshape(nb * block_size, cache.shape[1], cache.shape[3])
+        parts.append(seq[:int(L)])
+    return np.concatenate(parts, axis=0)

@@ -1,0 +1,451 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each check ties the oracle to the pages or to mathematics it cannot share a
+mistake with: an independent dense NumPy brute force, PyTorch's own
+scaled-dot-product attention for the special cases that reduce to it
+(no bias; ALiBi), closed forms, invariants, and the numbers the pages print
+(tests/golden). A mutation test at the end shows that plausible slips in the
+oracle (a dropped term, a reversed or shifted index, a wrong head map) are
+caught by these pins.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def make_case(rng, q_lens, seq_lens, Hq, Hkv, dqk, dv, R, scale_qk=1.0):
+    tq, tk = int(sum(q_lens)), int(sum(seq_lens))
+    return dict(
+        q=rng.standard_normal((tq, Hq, dqk)) * scale_qk,
+        k=rng.standard_normal((tk, Hkv, dqk)) * scale_qk,
+        v=rng.standard_normal((tk, Hkv, dv)),
+        rel=0.5 * rng.standard_normal((tq, Hq, R)),
+        q_lens=np.asarray(q_lens, dtype=np.int64),
+        seq_lens=np.asarray(seq_lens, dtype=np.int64),
+    )
+
+
+def run_oracle(c, R, W, scale, rows=None):
+    return oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"],
+                         rel_extent=R, window=W, scale=scale, rows=rows)
+
+
+def brute(c, R, W, scale):
+    """Dense float64 attention with explicit [Lq, L] mask and bias matrices,
+    written independently of the oracle (vectorised NumPy, no online softmax)."""
+    q, k, v, rel = c["q"], c["k"], c["v"], c["rel"]
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    outs, lses = [], []
+    q0 = k0 = 0
+    for Lq, L in zip(c["q_lens"], c["seq_lens"]):
+        Lq, L = int(Lq), int(L)
+        qi = np.arange(L - Lq, L)[:, None]          # absolute query positions
+        kj = np.arange(L)[None, :]
+        dist = qi - kj                              # [Lq, L]
+        visible = dist >= 0
+        if W > 0:
+            visible &= dist < W
+        in_extent = (dist >= 0) & (dist < R)
+        o = np.zeros((Lq, Hq, v.shape[2]))
+        ls = np.zeros((Lq, Hq))
+        for h in range(Hq):
+            g = h // G
+            S = scale * (q[q0:q0 + Lq, h] @ k[k0:k0 + L, g].T)
+            relh = rel[q0:q0 + Lq, h]                # [Lq, R]
+            B = np.where(in_extent, np.take_along_axis(relh, np.clip(dist, 0, R - 1), axis=1), 0.0)
+            X = np.where(visible, S + B, -np.inf)
+            m = X.max(axis=1, keepdims=True)
+            P = np.exp(X - m)
+            den = P.sum(axis=1, keepdims=True)
+            o[:, h] = (P / den) @ v[k0:k0 + L, g]
+            ls[:, h] = (m + np.log(den))[:, 0]
+        outs.append(o)
+        lses.append(ls)
+        q0 += Lq
+        k0 += L
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def sdpa_f64(q, k, v, mask, scale, G):
+    """torch scaled_dot_product_attention in float64 on the CPU.
+    q [Lq, Hq, d], k/v [L, Hkv, d], mask [Lq, L] (bool = attend, or additive float)."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+    tm = torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=tm, scale=scale, enable_gqa=(G > 1))
+    return o[0].permute(1, 0, 2).numpy()
+
+
+# ----------------------------------------------------------------------------
+# P1: brute force on tiny inputs
+# ----------------------------------------------------------------------------
+BRUTE_GRID = [
+    # q_lens, seq_lens, Hq, Hkv, dqk, dv, R, W
+    ([5], [5], 4, 1, 8, 8, 3, 0),
+    ([7, 3], [20, 3], 4, 2, 16, 8, 5, 4),
+    ([1, 1, 1], [9, 1, 17], 2, 2, 8, 16, 7, 0),
+    ([12], [40], 6, 2, 16, 4, 64, 6),
+    ([0, 9], [4, 30], 4, 4, 8, 8, 1, 1),
+    ([16], [16], 4, 1, 16, 16, 16, 16),
+    ([4, 6], [48, 80], 4, 1, 16, 8, 9, 20),
+    ([31], [47], 3, 1, 8, 8, 2, 33),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_GRID)
+def test_p1_brute_force(case):
+    q_lens, seq_lens, Hq, Hkv, dqk, dv, R, W = case
+    rng = np.random.default_rng(1234 + len(q_lens) + R + W)
+    c = make_case(rng, q_lens, seq_lens, Hq, Hkv, dqk, dv, R)
+    scale = 1.0 / math.sqrt(dqk)
+    o, l = run_oracle(c, R, W, scale)
+    ob, lb = brute(c, R, W, scale)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def test_p1_row_subset_matches_full():
+    rng = np.random.default_rng(7)
+    c = make_case(rng, [6, 10], [30, 12], 4, 2, 8, 8, 8, 5)
+    full, lfull = run_oracle(c, 8, 5, 0.3)
+    rows = [0, 3, 15, 7]
+    sub, lsub = run_oracle(c, 8, 5, 0.3, rows=rows)
+    np.testing.assert_array_equal(sub[rows], full[rows])
+    np.testing.assert_array_equal(lsub[rows], lfull[rows])
+    others = [r for r in range(16) if r not in rows]
+    assert np.isnan(sub[others]).all()
+
+
+# ----------------------------------------------------------------------------
+# P2: rel = 0 and no window is ordinary causal softmax attention
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("Lq,L,Hq,Hkv", [(24, 24, 4, 1), (10, 37, 4, 2), (1, 50, 8, 2), (16, 40, 2, 2)])
+def test_p2_rel_zero_is_causal_sdpa(Lq, L, Hq, Hkv):
+    rng = np.random.default_rng(Lq * 100 + L)
+    R = 5
+    c = make_case(rng, [Lq], [L], Hq, Hkv, 16, 8, R)
+    c["rel"][:] = 0.0
+    scale = 0.25
+    o, _ = run_oracle(c, R, 0, scale)
+    mask = np.arange(L)[None, :] <= np.arange(L - Lq, L)[:, None]
+    ref = sdpa_f64(c["q"], c["k"], c["v"], mask, scale, Hq // Hkv)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P3: local-window prefill over only the last blocks equals the full context
+# ----------------------------------------------------------------------------
+def truncated_to_window(c, W, bs):
+    """Keep only the blocks a window-W query chunk can see (one sequence);
+    positions shift by a whole number of blocks."""
+    Lq, L = int(c["q_lens"][0]), int(c["seq_lens"][0])
+    first = L - Lq
+    kb_lo = max(0, first - W + 1) // bs
+    drop = kb_lo * bs
+    t = dict(c)
+    t["k"] = c["k"][drop:]
+    t["v"] = c["v"][drop:]
+    t["seq_lens"] = np.asarray([L - drop], dtype=np.int64)
+    return t, kb_lo
+
+
+def test_p3_local_window_equivalence_40_cases():
+    g = json.load(open(os.path.join(GOLDEN, "local_window_blocks.json")))
+    rng = np.random.default_rng(40)
+    for case in range(g["random_cases"]):
+        bs = int(rng.choice([4, 8, 16]))
+        W = int(rng.integers(1, 6 * bs))
+        L = int(rng.integers(1, 12 * bs))
+        Lq = int(rng.integers(1, L + 1))
+        R = int(rng.integers(1, W + 3))
+        c = make_case(rng, [Lq], [L], 4, 2, 8, 8, R)
+        scale = float(rng.uniform(0.1, 0.5))
+        full, lf = run_oracle(c, R, W, scale)
+        t, _ = truncated_to_window(c, W, bs)
+        trunc, lt = run_oracle(t, R, W, scale)
+        np.testing.assert_array_equal(trunc, full, err_msg=f"case {case}")
+        np.testing.assert_array_equal(lt, lf, err_msg=f"case {case}")
+
+
+def test_p3_pages_five_blocks_for_window_512():
+    g = json.load(open(os.path.join(GOLDEN, "local_window_blocks.json")))
+    W, bs = g["window"], g["block_size"]
+    # a decode query at any position needs blocks floor((i-W+1)/bs) .. floor(i/bs)
+    need = max((i // bs) - (max(0, i - W + 1) // bs) + 1 for i in range(W, W + 4 * bs))
+    assert need == g["context_blocks_needed"]
+    assert need == -(-(W - 1) // bs) + 1
+    # and with that many blocks the output is unchanged (small head size)
+    rng = np.random.default_rng(5)
+    L, Lq = 3 * W + 77, 3
+    c = make_case(rng, [Lq], [L], 2, 1, 8, 4, W)
+    full, _ = run_oracle(c, W, W, 0.3)
+    t, kb_lo = truncated_to_window(c, W, bs)
+    assert (L + bs - 1) // bs - kb_lo <= need + 1   # the chunk's last query may start a block
+    trunc, _ = run_oracle(t, W, W, 0.3)
+    np.testing.assert_array_equal(trunc, full)
+
+
+# ----------------------------------------------------------------------------
+# P4: rel = -m_h * d is ALiBi
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("Lq,L", [(20, 20), (6, 33)])
+def test_p4_alibi_special_case(Lq, L):
+    rng = np.random.default_rng(Lq + 7 * L)
+    Hq, Hkv, R = 4, 2, L + 5          # R beyond every distance
+    c = make_case(rng, [Lq], [L], Hq, Hkv, 16, 8, R)
+    slopes = 2.0 ** (-np.arange(1, Hq + 1))
+    c["rel"] = np.broadcast_to(-slopes[None, :, None] * np.arange(R)[None, None, :], (Lq, Hq, R)).copy()
+    scale = 0.25
+    o, _ = run_oracle(c, R, 0, scale)
+    qi = np.arange(L - Lq, L)[:, None]
+    kj = np.arange(L)[None, :]
+    for h in range(Hq):
+        mask = np.where(kj <= qi, -slopes[h] * (qi - kj).astype(np.float64), -np.inf)
+        g = h // (Hq // Hkv)
+        ref = sdpa_f64(c["q"][:, h:h + 1], c["k"][:, g:g + 1], c["v"][:, g:g + 1], mask, scale, 1)
+        np.testing.assert_allclose(o[:, h:h + 1], ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P5: a one-hot bias selects exactly the key at distance d0
+# ----------------------------------------------------------------------------
+def test_p5_shear_index_probe():
+    rng = np.random.default_rng(55)
+    q_lens, seq_lens = [9, 4], [25, 60]
+    Hq, Hkv, R, W = 4, 2, 30, 24
+    c = make_case(rng, q_lens, seq_lens, Hq, Hkv, 8, 8, R)
+    c["q"][:] = 0
+    c["k"][:] = 0
+    c["rel"][:] = 0
+    expect = np.zeros((sum(q_lens), Hq, 8))
+    t = 0
+    k0 = 0
+    for Lq, L in zip(q_lens, seq_lens):
+        for r in range(Lq):
+            i = L - Lq + r
+            for h in range(Hq):
+                d0 = int(rng.integers(0, min(i + 1, W, R)))
+                c["rel"][t, h, d0] = 40.0
+                expect[t, h] = c["v"][k0 + i - d0, h // 2]
+            t += 1
+        k0 += L
+    o, _ = run_oracle(c, R, W, 0.3)
+    np.testing.assert_allclose(o, expect, rtol=0, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------
+# P6: window of exactly W keys including the query's own key
+# ----------------------------------------------------------------------------
+def test_p6_window_closed_form_and_boundary_probe():
+    rng = np.random.default_rng(66)
+    L, Lq, W, R = 70, 50, 16, 32
+    c = make_case(rng, [Lq], [L], 2, 1, 8, 8, R)
+    c["q"][:] = 0
+    c["k"][:] = 0
+    c["rel"][:] = 0
+    o, _ = run_oracle(c, R, W, 0.5)
+    for r in range(Lq):
+        i = L - Lq + r
+        lo = max(0, i - W + 1)
+        np.testing.assert_allclose(o[r, 0], c["v"][lo:i + 1, 0].mean(axis=0), rtol=0, atol=1e-12)
+    # d0 = W-1 is visible, d0 = W is not
+    for d0, visible in ((W - 1, True), (W, False)):
+        c2 = dict(c)
+        c2["rel"] = np.zeros_like(c["rel"])
+        c2["rel"][:, :, d0] = 40.0
+        o2, _ = run_oracle(c2, R, W, 0.5)
+        r = Lq - 1
+        i = L - 1
+        if visible:
+            np.testing.assert_allclose(o2[r, 0], c["v"][i - d0, 0], rtol=0, atol=1e-9)
+        else:
+            np.testing.assert_allclose(o2[r, 0], c["v"][i - W + 1:i + 1, 0].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_golden_decode_window_counts():
+    """The pages' decode-window numbers follow from the reading 'visible iff
+    0 <= i-j < W': a 4-block decode context shows 385..512 keys, 5 blocks
+    show exactly 512."""
+    g = json.load(open(os.path.join(GOLDEN, "decode_window.json")))
+    W, bs = g["window"], g["block_size"]
+
+    def count_visible(i, n_blocks):
+        # one decode query at position i whose context is the last n_blocks blocks
+        first_block = max(0, i // bs - (n_blocks - 1))
+        drop = first_block * bs
+        L = i + 1 - drop
+        kv = np.zeros((L, 1, 2))
+        kv[:, 0, 1] = np.arange(L)                  # value = position
+        c = dict(q=np.zeros((1, 1, 2)), k=np.zeros((L, 1, 2)), v=kv,
+                 rel=np.zeros((1, 1, W)), q_lens=np.array([1]), seq_lens=np.array([L]))
+        o, _ = run_oracle(c, W, W, 1.0)
+        mean_pos = o[0, 0, 1]
+        return int(round(2 * ((L - 1) - mean_pos) + 1))   # contiguous range ending at i
+
+    positions = range(4 * bs, 4 * bs + bs)                # every residue i mod 128
+    before = [count_visible(i, g["decode_blocks_before_fix"]) for i in positions]
+    after = [count_visible(i, g["decode_blocks_after_fix"]) for i in positions]
+    assert min(before) == g["visible_keys_before_fix"]["min"]
+    assert max(before) == g["visible_keys_before_fix"]["max"]
+    assert set(after) == {g["visible_keys_after_fix"]}
+
+
+def test_golden_kv_page_bytes():
+    g = json.load(open(os.path.join(GOLDEN, "kv_page_bytes.json")))
+    per_rank_heads = g["num_kv_heads"] // g["tensor_parallel"]
+    page = g["block_size"] * per_rank_heads * g["head_dim"] * g["bytes_per_element"] * g["tensors"]
+    assert page == g["page_bytes_per_block_per_layer"]
+
+
+# ----------------------------------------------------------------------------
+# P7: beyond the relative extent the bias is 0 (closed form)
+# ----------------------------------------------------------------------------
+def test_p7_beyond_extent_closed_form():
+    rng = np.random.default_rng(77)
+    L, Lq, R, cst = 60, 20, 12, 1.7
+    c = make_case(rng, [Lq], [L], 2, 1, 8, 8, R)
+    c["q"][:] = 0
+    c["k"][:] = 0
+    c["rel"][:] = cst
+    o, _ = run_oracle(c, R, 0, 0.5)
+    v = c["v"][:, 0]
+    for r in range(Lq):
+        i = L - Lq + r
+        n = i + 1
+        near = v[i - min(R, n) + 1:i + 1].sum(axis=0)      # distances < R
+        far = v[:max(0, n - R)].sum(axis=0)                 # distances >= R
+        den = min(R, n) * math.exp(cst) + max(0, n - R)
+        np.testing.assert_allclose(o[r, 0], (math.exp(cst) * near + far) / den, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P8: adding a per-row constant to rel leaves the output unchanged
+# ----------------------------------------------------------------------------
+def test_p8_row_shift_invariance():
+    rng = np.random.default_rng(88)
+    c = make_case(rng, [10, 5], [30, 41], 4, 2, 8, 8, 64)
+    o, l = run_oracle(c, 64, 0, 0.3)
+    shift = rng.uniform(-3, 3, size=c["rel"].shape[:2])
+    c2 = dict(c)
+    c2["rel"] = c["rel"] + shift[:, :, None]
+    o2, l2 = run_oracle(c2, 64, 0, 0.3)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l + shift, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P9: chunked prefill and decode rows equal the one-shot prefill rows
+# ----------------------------------------------------------------------------
+def test_p9_chunking_and_decode_rows():
+    rng = np.random.default_rng(99)
+    L, R, W = 48, 10, 0
+    full = make_case(rng, [L], [L], 4, 2, 8, 8, R)
+    o_full, l_full = run_oracle(full, R, W, 0.3)
+    for cuts in ([0, 12, 30, 48], [0, 47, 48], [0, 16, 32, 48]):
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            ch = dict(q=full["q"][a:b], k=full["k"][:b], v=full["v"][:b], rel=full["rel"][a:b],
+                      q_lens=np.array([b - a]), seq_lens=np.array([b]))
+            o, l = run_oracle(ch, R, W, 0.3)
+            np.testing.assert_array_equal(o, o_full[a:b])
+            np.testing.assert_array_equal(l, l_full[a:b])
+
+
+# ----------------------------------------------------------------------------
+# P10: GQA head map h -> h // G
+# ----------------------------------------------------------------------------
+def test_p10_gqa_replication():
+    rng = np.random.default_rng(1010)
+    Hq, Hkv = 6, 2
+    c = make_case(rng, [7], [19], Hq, Hkv, 8, 8, 6)
+    o, _ = run_oracle(c, 6, 5, 0.3)
+    rep = dict(c)
+    rep["k"] = np.repeat(c["k"], Hq // Hkv, axis=1)
+    rep["v"] = np.repeat(c["v"], Hq // Hkv, axis=1)
+    o2, _ = run_oracle(rep, 6, 5, 0.3)
+    np.testing.assert_array_equal(o2, o)
+
+
+# ----------------------------------------------------------------------------
+# P11: a narrower value head is a column slice
+# ----------------------------------------------------------------------------
+def test_p11_diff_headdim_is_column_slice():
+    rng = np.random.default_rng(1111)
+    c = make_case(rng, [9], [21], 4, 1, 16, 8, 7)
+    o, l = run_oracle(c, 7, 0, 0.25)
+    wide = dict(c)
+    wide["v"] = np.concatenate([c["v"], rng.standard_normal(c["v"].shape)], axis=2)
+    ow, lw = run_oracle(wide, 7, 0, 0.25)
+    np.testing.assert_array_equal(ow[:, :, :8], o)
+    np.testing.assert_array_equal(lw, l)
+
+
+def test_degenerate_single_key_and_extent_one():
+    rng = np.random.default_rng(3)
+    c = make_case(rng, [4], [9], 2, 1, 8, 8, 1)
+    o, l = run_oracle(c, 1, 1, 0.3)         # W = 1: only the query's own key
+    np.testing.assert_allclose(o[:, 0], c["v"][5:9, 0], rtol=0, atol=0)
+    qk = 0.3 * np.einsum("td,td->t", c["q"][:, 0], c["k"][5:9, 0])
+    np.testing.assert_allclose(l[:, 0], qk + c["rel"][:, 0, 0], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Mutation check: planted slips in the oracle (on the CPU) must fail a pin
+# ----------------------------------------------------------------------------
+MUTANTS = {
+    "dropped_bias": ("x[j - lo] = scale * s + bias;", "x[j - lo] = scale * s;"),
+    "reversed_distance": ("relr[dist] : 0.0", "relr[R - 1 - dist] : 0.0"),
+    "clamped_beyond_extent": ("relr[dist] : 0.0", "relr[dist] : relr[R - 1]"),
+    "window_off_by_one": ("i - W + 1 > 0 ? i - W + 1 : 0", "i - W > 0 ? i - W : 0"),
+    "head_map_modulo": ("const int64_t g = h / G;", "const int64_t g = h % Hkv;"),
+    "dropped_scale": ("x[j - lo] = scale * s + bias;", "x[j - lo] = s + bias;"),
+    "key_offset": ("(kv_start[b] + j) * Hkv + g) * dqk", "(kv_start[b] + j + (j > 0 ? -1 : 0)) * Hkv + g) * dqk"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_are_caught(name, monkeypatch):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, name
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "m.c")
+        open(path, "w").write(src.replace(old, new))
+        so = os.path.join(d, "libm.so")
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", path, "-o", so, "-lm"], check=True)
+        lib = ctypes.CDLL(so)
+        i64, dbl, P = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.rba_oracle_attend.argtypes = [i64, P, P, i64, i64, i64, i64, i64, i64, dbl,
+                                          P, P, P, P, P, i64, P, P]
+        lib.rba_oracle_attend.restype = ctypes.c_int
+        monkeypatch.setattr(oracle, "_lib", lib)
+        caught = False
+        for case in BRUTE_GRID:
+            q_lens, seq_lens, Hq, Hkv, dqk, dv, R, W = case
+            rng = np.random.default_rng(1234 + len(q_lens) + R + W)
+            c = make_case(rng, q_lens, seq_lens, Hq, Hkv, dqk, dv, R)
+            scale = 1.0 / math.sqrt(dqk)
+            o, l = run_oracle(c, R, W, scale)
+            ob, lb = brute(c, R, W, scale)
+            if not (np.allclose(o, ob, rtol=0, atol=1e-12) and np.allclose(l, lb, rtol=0, atol=1e-12)):
+                caught = True
+                break
+        assert caught, f"mutant {name} passed the brute-force pin"
