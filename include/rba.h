@@ -1,0 +1,226 @@
+/*
+ * librba — relative-bias grouped-query attention on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the method, restated from the pages):
+ *   "Inkling-Small on Gaudi 2", sections "Why it needed a port" and
+ *   "Attention with a relative bias": every attention logit gets a learned
+ *   per-query, per-head, per-distance term rel[i, h, i - j] in place of RoPE;
+ *   rel is produced for the tokens of the current call (one row per query
+ *   token) and handed to the attention call; chunked prefill and prefix hits
+ *   attend to the cached context plus the new tokens; key positions in a paged
+ *   cache are block ordinal * block size + slot.
+ *   Same page, "What was built": GQA (32 query / 8 KV heads, head size 128),
+ *   local layers with a 512-token window (relative extent 512), global layers
+ *   without a window (relative extent 1024).
+ *   Same page, "Decode window": the window holds exactly W keys including the
+ *   query's own key.
+ *   "Inkling on Two DGX Sparks ...", section "Wall 1": the value head size may
+ *   differ from the query/key head size (128 vs 64); decode splits the KV range
+ *   and must not read device values on the host (graph capture).
+ *   "vLLM TML Inkling Support", section "Low-Latency Collectives and Kernels":
+ *   the number of KV splits is chosen from batch size and KV length.
+ *   "Inkling 2 Small on vLLM: Day-0 Support", integration section: decode and
+ *   verify read each KV block once for all query heads that share it.
+ *
+ *   For query row t (absolute position i) of sequence b, query head h, KV head
+ *   g = h / (Hq / Hkv):
+ *     x_j      = scale * <q[t,h,:], K_b[j,g,:]> + (i - j < R ? rel[t,h,i-j] : 0)
+ *     visible  = j <= i  and  (W == 0 or i - j < W)
+ *     out[t,h] = sum_j softmax_j(x) * V_b[j,g,:]      (fp32)
+ *     lse[t,h] = log sum_j exp(x_j)                   (fp32, natural log)
+ *   The bias for distances i - j >= R is 0: the pages do not define it and this
+ *   library fixes it to zero.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers are device memory owned by the caller;
+ *     the library allocates nothing, frees nothing and keeps no pointer after
+ *     the call returns. `params` and other host pointers are read during the
+ *     call only.
+ *   - Layouts are dense row-major. bf16 is IEEE bfloat16 (uint16 storage).
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without waiting. No call reads device memory on the host, so
+ *     calls may be captured into a HIP graph. Calls are thread-safe.
+ *   - All argument checks run on the host before anything is launched; a call
+ *     that returns an error has enqueued nothing and written nothing.
+ *   - Return 0 on success or a negative RBA_ERR_* code; rba_last_error()
+ *     then describes the problem (thread-local).
+ *   - Values the library cannot check without reading device memory are the
+ *     caller's contract (undefined results, never out-of-bounds accesses, if
+ *     violated): q_len_b <= seq_lens[b] <= max_seq_len, cu_q non-decreasing,
+ *     and q_len_b <= max_q_len. Table entries for blocks a query can see must
+ *     be in [0, num_blocks); an entry outside that range makes the affected
+ *     rows NaN instead of being dereferenced. Entries for blocks that no query
+ *     of the call can see (wholly outside every window) are never read and
+ *     may hold anything, e.g. -1.
+ *   - Slots of the last block past seq_lens[b] are never used: whatever they
+ *     hold (NaN included) contributes exactly 0.
+ */
+#ifndef RBA_H
+#define RBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RBA_OK 0
+#define RBA_ERR_NULL (-1)        /* a required pointer is NULL                      */
+#define RBA_ERR_SHAPE (-2)       /* inconsistent sizes or counts                     */
+#define RBA_ERR_UNSUPPORTED (-3) /* valid in principle, not supported by the kernels */
+#define RBA_ERR_WORKSPACE (-4)   /* workspace missing or too small                   */
+#define RBA_ERR_HIP (-5)         /* a HIP runtime call failed                        */
+
+#define RBA_BLOCK_SIZE 128       /* tokens per KV-cache block                        */
+#define RBA_HEAD_DIM_QK 128      /* supported query/key head size                    */
+
+typedef struct rba_attn_params {
+    int32_t num_heads_q;   /* Hq >= 1                                                */
+    int32_t num_heads_kv;  /* Hkv >= 1, Hq % Hkv == 0; query head h uses KV head    */
+                           /* h / (Hq / Hkv)                                         */
+    int32_t head_dim_qk;   /* must be 128                                            */
+    int32_t head_dim_v;    /* 64 or 128                                              */
+    int32_t rel_extent;    /* R: bias defined for distances 0 <= i-j < R, 0 beyond;  */
+                           /* R >= 4 and R % 4 == 0                                  */
+    int32_t window;        /* W: 0 = no window; else key visible iff 0 <= i-j < W    */
+    float scale;           /* finite multiplier of q.k (e.g. 1/sqrt(128))            */
+    int32_t block_size;    /* must be RBA_BLOCK_SIZE                                 */
+} rba_attn_params;
+
+/* Library version string, e.g. "librba 0.1.0 gfx950". */
+const char* rba_version(void);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* rba_last_error(void);
+
+/*
+ * Prefill / chunked prefill / prefix-cache extension.
+ * Source: "Inkling-Small on Gaudi 2", section "Attention with a relative
+ * bias" (a chunk attends to all cached context plus itself; key positions
+ * from block ordinals; local layers need only the blocks inside the window).
+ *
+ *   q            device bf16 [total_q, Hq, 128]; rows of all sequences packed,
+ *                sequence b owns rows [cu_q[b], cu_q[b+1])
+ *   k_cache      device bf16 [num_blocks, Hkv, 128, 128]   (block, head, slot, dim)
+ *   v_cache      device bf16 [num_blocks, Hkv, 128, dv]
+ *   num_blocks   number of blocks in the cache pool (>= 1)
+ *   rel          device fp32 [total_q, Hq, R]; row t is the bias row of query row t
+ *   cu_q         device int32 [batch + 1]; query-row offsets, cu_q[0] = 0
+ *   seq_lens     device int32 [batch]; keys of sequence b INCLUDING this call's
+ *                tokens, whose K/V must already be in the cache. The query rows
+ *                of b are its last q_len_b = cu_q[b+1]-cu_q[b] positions.
+ *   block_tables device int32 [batch, max_blocks_per_seq]; entry n is the physical
+ *                block holding positions [128 n, 128 n + 128) of the sequence
+ *   batch        number of sequences (0 = nothing to do)
+ *   max_q_len    host upper bound of every q_len_b (sets the grid)
+ *   max_seq_len  host upper bound of every seq_lens[b]; max_blocks_per_seq must be
+ *                >= ceil(max_seq_len / 128)
+ *   out          device fp32 [total_q, Hq, dv]  (written)
+ *   lse          device fp32 [total_q, Hq] or NULL (written if non-NULL)
+ *   stream       hipStream_t
+ * Errors: RBA_ERR_NULL, RBA_ERR_SHAPE, RBA_ERR_UNSUPPORTED, RBA_ERR_HIP.
+ */
+int rba_prefill(const rba_attn_params* params,
+                const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                float* out, float* lse, void* stream);
+
+/* Host-only argument check of rba_prefill (no HIP call; same return codes). */
+int rba_validate_prefill(const rba_attn_params* params,
+                         const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                         const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                         const float* out);
+
+/*
+ * Paged decode / speculative verify with split-KV and a log-sum-exp combine.
+ * Sources: "Inkling-Small on Gaudi 2", section "Attention with a relative
+ * bias" (decode keys at block-ordinal positions); "vLLM TML Inkling Support",
+ * section "Low-Latency Collectives and Kernels" (split count chosen from batch
+ * and KV length); "Inkling on Two DGX Sparks ...", section "Wall 1" (split-KV
+ * decode, dv may be 64, no device-to-host reads); "Inkling 2 Small on vLLM:
+ * Day-0 Support", integration section (each KV block read once for all query
+ * heads sharing it; several verify tokens per sequence).
+ *
+ *   q            device bf16 [batch * n_q, Hq, 128]; row b*n_q + u is token u of
+ *                sequence b, at position seq_lens[b] - n_q + u
+ *   k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq: as rba_prefill
+ *   rel          device fp32 [batch * n_q, Hq, R]
+ *   seq_lens     device int32 [batch]; includes the n_q new tokens (n_q <= seq_lens[b])
+ *   n_q          query tokens per sequence, 1 <= n_q and G * n_q <= 256
+ *                (G = Hq / Hkv); causal among themselves
+ *   max_seq_len  host upper bound of seq_lens (sets the split plan and the grid)
+ *   num_splits   0 = automatic (rba_decode_plan_splits with this device's CU
+ *                count), else 1 <= num_splits <= 1024
+ *   workspace    device memory of at least rba_decode_workspace_size(...) bytes
+ *                (partial outputs; contents on entry are ignored)
+ *   out          device fp32 [batch * n_q, Hq, dv]; lse device fp32 [batch*n_q, Hq]
+ *                or NULL
+ * Errors: RBA_ERR_NULL, RBA_ERR_SHAPE, RBA_ERR_UNSUPPORTED, RBA_ERR_WORKSPACE,
+ * RBA_ERR_HIP.
+ */
+int rba_decode(const rba_attn_params* params,
+               const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+               const float* rel, const int32_t* seq_lens,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+               void* workspace, size_t workspace_bytes,
+               float* out, float* lse, void* stream);
+
+/* Host-only argument check of rba_decode (no HIP call; same return codes). */
+int rba_validate_decode(const rba_attn_params* params,
+                        const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                        const float* rel, const int32_t* seq_lens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                        const void* workspace, size_t workspace_bytes, const float* out);
+
+/*
+ * Split plan (host only, pure function). Returns the number of KV splits
+ * rba_decode uses for num_splits = 0 on a device with `num_cus` compute units:
+ * enough (sequence, KV head, split) work units to give every CU several, no
+ * more splits than KV blocks, at most 256. Returns a negative RBA_ERR_* code on
+ * bad arguments.
+ */
+int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                               int32_t max_seq_len, int32_t num_cus);
+
+/*
+ * Bytes of workspace rba_decode needs (host only). num_splits = 0 plans with
+ * the current device's CU count (256 when no device is visible). Returns 0 on
+ * bad arguments.
+ * Layout: fp32 partial outputs [batch*n_q, Hq, splits, dv] followed by fp32
+ * partial log-sum-exp [batch*n_q, Hq, splits].
+ */
+size_t rba_decode_workspace_size(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                                 int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * The two stages of rba_decode, callable one at a time (rba_decode is exactly
+ * rba_decode_split followed by rba_decode_combine on the same stream).
+ * rba_decode_split writes, for every (row, head, split), the split's
+ * normalised partial output and its log-sum-exp into `workspace` (a split
+ * that sees no key gets lse = -inf). rba_decode_combine merges them:
+ *   LSE = log sum_s exp(lse_s),  out = sum_s exp(lse_s - LSE) * O_s.
+ * `num_splits` must be the resolved count (>= 1) for both calls.
+ */
+int rba_decode_split(const rba_attn_params* params,
+                     const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                     const float* rel, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                       int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                       float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBA_H */

@@ -1,0 +1,401 @@
+// Host side of librba: argument validation, the split plan, workspace sizing
+// and the C-ABI entry points declared in include/rba.h. Validation and
+// planning are pure host code (no HIP call), so they can be exercised on a
+// machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rba.h"
+#include "rba_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return RBA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_params(const rba_attn_params* p) {
+    if (p == nullptr) return fail(RBA_ERR_NULL, "params is NULL");
+    if (p->num_heads_q < 1 || p->num_heads_kv < 1)
+        return fail(RBA_ERR_SHAPE, "num_heads_q (%d) and num_heads_kv (%d) must be >= 1",
+                    p->num_heads_q, p->num_heads_kv);
+    if (p->num_heads_q % p->num_heads_kv != 0)
+        return fail(RBA_ERR_SHAPE, "num_heads_q (%d) is not a multiple of num_heads_kv (%d)",
+                    p->num_heads_q, p->num_heads_kv);
+    if (p->head_dim_qk != RBA_HEAD_DIM_QK)
+        return fail(RBA_ERR_UNSUPPORTED, "head_dim_qk %d unsupported (must be 128)", p->head_dim_qk);
+    if (p->head_dim_v != 64 && p->head_dim_v != 128)
+        return fail(RBA_ERR_UNSUPPORTED, "head_dim_v %d unsupported (64 or 128)", p->head_dim_v);
+    if (p->rel_extent < 1) return fail(RBA_ERR_SHAPE, "rel_extent %d must be >= 1", p->rel_extent);
+    if (p->rel_extent % 4 != 0)
+        return fail(RBA_ERR_UNSUPPORTED, "rel_extent %d unsupported (must be a multiple of 4)",
+                    p->rel_extent);
+    if (p->window < 0) return fail(RBA_ERR_SHAPE, "window %d must be >= 0", p->window);
+    if (!isfinite(p->scale)) return fail(RBA_ERR_SHAPE, "scale is not finite");
+    if (p->block_size != RBA_BLOCK_SIZE)
+        return fail(RBA_ERR_UNSUPPORTED, "block_size %d unsupported (must be 128)", p->block_size);
+    return RBA_OK;
+}
+
+int check_cache(const void* k_cache, const void* v_cache, int32_t num_blocks,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t max_seq_len) {
+    if (k_cache == nullptr || v_cache == nullptr) return fail(RBA_ERR_NULL, "k_cache/v_cache is NULL");
+    if (block_tables == nullptr) return fail(RBA_ERR_NULL, "block_tables is NULL");
+    if (num_blocks < 1) return fail(RBA_ERR_SHAPE, "num_blocks %d must be >= 1", num_blocks);
+    if (max_seq_len > INT32_MAX - 2 * RBA_BLOCK_SIZE)
+        return fail(RBA_ERR_UNSUPPORTED, "max_seq_len %d too large", max_seq_len);
+    if (max_blocks_per_seq < ceil_div(max_seq_len, RBA_BLOCK_SIZE))
+        return fail(RBA_ERR_SHAPE, "max_blocks_per_seq %d < ceil(max_seq_len %d / 128)",
+                    max_blocks_per_seq, max_seq_len);
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(RBA_ERR_UNSUPPORTED, "k_cache/v_cache must be 16-byte aligned");
+    if (!aligned4(block_tables)) return fail(RBA_ERR_UNSUPPORTED, "block_tables must be 4-byte aligned");
+    return RBA_OK;
+}
+
+// Query heads per prefill workgroup: the largest of 8, 4, 2, 1 dividing G.
+int prefill_hpw(int G) {
+    for (int h = 8; h > 1; h >>= 1)
+        if (G % h == 0) return h;
+    return 1;
+}
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+int64_t decode_nb_eff(const rba_attn_params* p, int32_t n_q, int32_t max_seq_len) {
+    const int64_t nb_max = ceil_div(max_seq_len, RBA_BLOCK_SIZE);
+    if (p->window == 0) return nb_max;
+    const int64_t span = ceil_div((int64_t)p->window + n_q - 1, RBA_BLOCK_SIZE) + 1;
+    return span < nb_max ? span : nb_max;
+}
+
+int32_t plan_splits(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                    int32_t num_cus) {
+    const int64_t G = p->num_heads_q / p->num_heads_kv;
+    const int64_t n_cg = ceil_div(G * n_q, 32);
+    const int64_t nb_eff = decode_nb_eff(p, n_q, max_seq_len);
+    const int64_t units = (int64_t)batch * p->num_heads_kv * n_cg;
+    int64_t want = ceil_div(8LL * num_cus, units);
+    int64_t cap = ceil_div(nb_eff, 16);  // keep at least ~16 blocks per split
+    if (cap > 256) cap = 256;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    return (int32_t)want;
+}
+
+int check_decode_shape(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t max_seq_len) {
+    if (batch < 0) return fail(RBA_ERR_SHAPE, "batch %d must be >= 0", batch);
+    if (n_q < 1) return fail(RBA_ERR_SHAPE, "n_q %d must be >= 1", n_q);
+    const int64_t G = p->num_heads_q / p->num_heads_kv;
+    if (G * n_q > 256)
+        return fail(RBA_ERR_UNSUPPORTED, "G * n_q = %lld exceeds 256", (long long)(G * n_q));
+    if (max_seq_len < n_q) return fail(RBA_ERR_SHAPE, "max_seq_len %d < n_q %d", max_seq_len, n_q);
+    return RBA_OK;
+}
+
+size_t ws_bytes(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t splits) {
+    const size_t pairs = (size_t)batch * n_q * p->num_heads_q;
+    return pairs * (size_t)splits * ((size_t)p->head_dim_v + 1) * sizeof(float);
+}
+
+int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cache, const void* v_cache,
+                     int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch,
+                     int32_t max_q_len, int32_t max_seq_len, const float* out, const float* lse,
+                     bool* nothing) {
+    *nothing = false;
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (batch < 0) return fail(RBA_ERR_SHAPE, "batch %d must be >= 0", batch);
+    if (max_q_len < 0) return fail(RBA_ERR_SHAPE, "max_q_len %d must be >= 0", max_q_len);
+    if (max_seq_len < max_q_len)
+        return fail(RBA_ERR_SHAPE, "max_seq_len %d < max_q_len %d", max_seq_len, max_q_len);
+    if (batch == 0 || max_q_len == 0) {
+        *nothing = true;
+        return ok();
+    }
+    if (q == nullptr || rel == nullptr || out == nullptr) return fail(RBA_ERR_NULL, "q/rel/out is NULL");
+    if (cu_q == nullptr || seq_lens == nullptr) return fail(RBA_ERR_NULL, "cu_q/seq_lens is NULL");
+    rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
+    if (rc) return rc;
+    if (!aligned16(q) || !aligned16(rel) || !aligned16(out))
+        return fail(RBA_ERR_UNSUPPORTED, "q/rel/out must be 16-byte aligned");
+    if (!aligned4(cu_q) || !aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
+        return fail(RBA_ERR_UNSUPPORTED, "cu_q/seq_lens/lse must be 4-byte aligned");
+    const int G = p->num_heads_q / p->num_heads_kv;
+    const int hpw = prefill_hpw(G);
+    const int64_t QT = 32LL * (8 / hpw);
+    const int64_t grid = (int64_t)batch * ceil_div(max_q_len, QT) * p->num_heads_kv * (G / hpw);
+    if (grid > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "launch too large (%lld workgroups)", (long long)grid);
+    return ok();
+}
+
+int validate_decode(const rba_attn_params* p, const void* q, const void* k_cache, const void* v_cache,
+                    int32_t num_blocks, const float* rel, const int32_t* seq_lens,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
+                    int32_t max_seq_len, int32_t num_splits, const void* workspace,
+                    size_t workspace_bytes, const float* out, const float* lse, bool need_out,
+                    int32_t* splits_out, bool* nothing) {
+    *nothing = false;
+    int rc = check_params(p);
+    if (rc) return rc;
+    rc = check_decode_shape(p, batch, n_q, max_seq_len);
+    if (rc) return rc;
+    if (num_splits < 0 || num_splits > 1024)
+        return fail(RBA_ERR_SHAPE, "num_splits %d out of range [0, 1024]", num_splits);
+    if (batch == 0) {
+        *nothing = true;
+        return ok();
+    }
+    if (q == nullptr || rel == nullptr || seq_lens == nullptr) return fail(RBA_ERR_NULL, "q/rel/seq_lens is NULL");
+    if (need_out && out == nullptr) return fail(RBA_ERR_NULL, "out is NULL");
+    rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
+    if (rc) return rc;
+    if (!aligned16(q) || !aligned16(rel) || (need_out && !aligned16(out)))
+        return fail(RBA_ERR_UNSUPPORTED, "q/rel/out must be 16-byte aligned");
+    if (!aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
+        return fail(RBA_ERR_UNSUPPORTED, "seq_lens/lse must be 4-byte aligned");
+    const int32_t splits = num_splits ? num_splits : plan_splits(p, batch, n_q, max_seq_len, device_cus());
+    const size_t need = ws_bytes(p, batch, n_q, splits);
+    if (workspace == nullptr) return fail(RBA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(RBA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(RBA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    const int64_t G = p->num_heads_q / p->num_heads_kv;
+    const int64_t grid = (int64_t)batch * p->num_heads_kv * ceil_div(G * n_q, 32) * splits;
+    if (grid > INT32_MAX) return fail(RBA_ERR_UNSUPPORTED, "launch too large (%lld workgroups)", (long long)grid);
+    if ((int64_t)batch * n_q * p->num_heads_q * splits > INT32_MAX)
+        return fail(RBA_ERR_UNSUPPORTED, "too many partial rows");
+    *splits_out = splits;
+    return ok();
+}
+
+rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void* k_cache,
+                            const void* v_cache, int32_t num_blocks, const float* rel,
+                            const int32_t* seq_lens, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                            int32_t splits, void* workspace) {
+    rba::DecodeArgs a;
+    const int G = p->num_heads_q / p->num_heads_kv;
+    const size_t pairs = (size_t)batch * n_q * p->num_heads_q;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.rel = rel;
+    a.seq_lens = seq_lens;
+    a.tables = block_tables;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = static_cast<float*>(workspace) + pairs * splits * p->head_dim_v;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.batch = batch;
+    a.Hq = p->num_heads_q;
+    a.Hkv = p->num_heads_kv;
+    a.G = G;
+    a.R = p->rel_extent;
+    a.W = p->window;
+    a.c1 = (float)((double)p->scale * 1.4426950408889634);
+    a.n_q = n_q;
+    a.n_cg = (int32_t)ceil_div((int64_t)G * n_q, 32);
+    a.splits = splits;
+    a.bps = (int32_t)ceil_div(decode_nb_eff(p, n_q, max_seq_len), splits);
+    return a;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(RBA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rba_version(void) { return "librba 0.1.0 gfx950"; }
+
+const char* rba_last_error(void) { return g_err; }
+
+int rba_validate_prefill(const rba_attn_params* params, const void* q, const void* k_cache,
+                         const void* v_cache, int32_t num_blocks, const float* rel, const int32_t* cu_q,
+                         const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         int32_t batch, int32_t max_q_len, int32_t max_seq_len, const float* out) {
+    bool nothing;
+    return validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                            max_blocks_per_seq, batch, max_q_len, max_seq_len, out, nullptr, &nothing);
+}
+
+int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                int32_t max_seq_len, float* out, float* lse, void* stream) {
+    bool nothing;
+    int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing);
+    if (rc || nothing) return rc;
+    rba::PrefillArgs a;
+    const int G = params->num_heads_q / params->num_heads_kv;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.rel = rel;
+    a.cu_q = cu_q;
+    a.seq_lens = seq_lens;
+    a.tables = block_tables;
+    a.out = out;
+    a.lse = lse;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.batch = batch;
+    a.Hq = params->num_heads_q;
+    a.Hkv = params->num_heads_kv;
+    a.G = G;
+    a.R = params->rel_extent;
+    a.W = params->window;
+    a.c1 = (float)((double)params->scale * 1.4426950408889634);
+    a.hpw = prefill_hpw(G);
+    a.QT = 32 * (8 / a.hpw);
+    a.n_qt = (int32_t)ceil_div(max_q_len, a.QT);
+    a.n_hc = G / a.hpw;
+    hipError_t e = rba::launch_prefill(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
+int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                               int32_t max_seq_len, int32_t num_cus) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    rc = check_decode_shape(params, batch, n_q, max_seq_len);
+    if (rc) return rc;
+    if (batch < 1) return fail(RBA_ERR_SHAPE, "batch must be >= 1 to plan");
+    if (num_cus < 1) return fail(RBA_ERR_SHAPE, "num_cus %d must be >= 1", num_cus);
+    ok();
+    return plan_splits(params, batch, n_q, max_seq_len, num_cus);
+}
+
+size_t rba_decode_workspace_size(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                                 int32_t max_seq_len, int32_t num_splits) {
+    if (check_params(params)) return 0;
+    if (check_decode_shape(params, batch, n_q, max_seq_len)) return 0;
+    if (num_splits < 0 || num_splits > 1024) return 0;
+    if (batch == 0) return 0;
+    const int32_t splits = num_splits ? num_splits : plan_splits(params, batch, n_q, max_seq_len, device_cus());
+    return ws_bytes(params, batch, n_q, splits);
+}
+
+int rba_validate_decode(const rba_attn_params* params, const void* q, const void* k_cache,
+                        const void* v_cache, int32_t num_blocks, const float* rel, const int32_t* seq_lens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
+                        int32_t max_seq_len, int32_t num_splits, const void* workspace,
+                        size_t workspace_bytes, const float* out) {
+    bool nothing;
+    int32_t splits = 0;
+    return validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                           max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                           workspace_bytes, out, nullptr, true, &splits, &nothing);
+}
+
+int rba_decode_split(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                     int32_t num_blocks, const float* rel, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
+                     int32_t max_seq_len, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (num_splits < 1) return fail(RBA_ERR_SHAPE, "rba_decode_split needs a resolved num_splits >= 1");
+    bool nothing;
+    int32_t splits = 0;
+    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                             workspace_bytes, nullptr, nullptr, false, &splits, &nothing);
+    if (rc || nothing) return rc;
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return ok();
+}
+
+int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q, int32_t num_splits,
+                       const void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+    int rc = check_params(params);
+    if (rc) return rc;
+    if (batch < 0 || n_q < 1) return fail(RBA_ERR_SHAPE, "batch %d / n_q %d invalid", batch, n_q);
+    if (num_splits < 1 || num_splits > 1024)
+        return fail(RBA_ERR_SHAPE, "num_splits %d out of range [1, 1024]", num_splits);
+    if (batch == 0) return ok();
+    if (out == nullptr) return fail(RBA_ERR_NULL, "out is NULL");
+    const size_t need = ws_bytes(params, batch, n_q, num_splits);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(RBA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace) || !aligned16(out) || (lse != nullptr && !aligned4(lse)))
+        return fail(RBA_ERR_UNSUPPORTED, "workspace/out must be 16-byte aligned, lse 4-byte");
+    const int64_t pairs = (int64_t)batch * n_q * params->num_heads_q;
+    if (pairs > INT32_MAX - 3) return fail(RBA_ERR_UNSUPPORTED, "too many rows");
+    rba::CombineArgs a;
+    a.part_o = static_cast<const float*>(workspace);
+    a.part_lse = static_cast<const float*>(workspace) + (size_t)pairs * num_splits * params->head_dim_v;
+    a.out = out;
+    a.lse = lse;
+    a.pairs = (int32_t)pairs;
+    a.splits = num_splits;
+    hipError_t e = rba::launch_combine(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+               int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+               int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+               void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+    bool nothing;
+    int32_t splits = 0;
+    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                             workspace_bytes, out, lse, true, &splits, &nothing);
+    if (rc || nothing) return rc;
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+}  // extern "C"

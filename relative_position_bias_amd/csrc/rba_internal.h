@@ -1,0 +1,60 @@
+// Internal interface between the host entry points (rba_host.cpp) and the
+// gfx950 kernels (rba_kernels.hip). Not installed; not part of the C ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace rba {
+
+// One prefill launch: work unit = (sequence, query tile, KV head, head chunk).
+struct PrefillArgs {
+    const uint16_t* q;        // bf16 [total_q, Hq, 128]
+    const uint16_t* k;        // bf16 [num_blocks, Hkv, 128, 128]
+    const uint16_t* v;        // bf16 [num_blocks, Hkv, 128, dv]
+    const float* rel;         // fp32 [total_q, Hq, R]
+    const int32_t* cu_q;      // [batch + 1]
+    const int32_t* seq_lens;  // [batch]
+    const int32_t* tables;    // [batch, max_blocks]
+    float* out;               // fp32 [total_q, Hq, dv]
+    float* lse;               // fp32 [total_q, Hq] or null
+    int32_t num_blocks, max_blocks, batch;
+    int32_t Hq, Hkv, G, R, W;
+    float c1;                 // scale * log2(e)
+    int32_t hpw;              // query heads per workgroup (divides G)
+    int32_t QT;               // query rows per tile = 32 * (8 / hpw)
+    int32_t n_qt;             // query tiles per sequence (from the host max_q_len)
+    int32_t n_hc;             // head chunks = G / hpw
+};
+
+// One split-KV decode launch: work unit = (sequence, KV head, column group, split).
+struct DecodeArgs {
+    const uint16_t* q;        // bf16 [batch * n_q, Hq, 128]
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* rel;         // fp32 [batch * n_q, Hq, R]
+    const int32_t* seq_lens;
+    const int32_t* tables;
+    float* part_o;            // fp32 [batch * n_q, Hq, splits, dv]
+    float* part_lse;          // fp32 [batch * n_q, Hq, splits]
+    int32_t num_blocks, max_blocks, batch;
+    int32_t Hq, Hkv, G, R, W;
+    float c1;
+    int32_t n_q, n_cg, splits, bps;   // column groups of 32 (head, token) pairs; blocks per split
+};
+
+struct CombineArgs {
+    const float* part_o;
+    const float* part_lse;
+    float* out;
+    float* lse;
+    int32_t pairs;            // batch * n_q * Hq
+    int32_t splits;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s);
+
+}  // namespace rba

@@ -1,0 +1,236 @@
+"""ctypes binding over librba.so: argument marshalling only.
+
+Every step of the attention runs in the library's gfx950 kernels; this module
+checks torch dtypes/devices/shapes, passes raw pointers and the current HIP
+stream, and raises if the library reports an error. It never computes
+attention itself and has no fallback: if librba.so is missing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librba.so")
+
+RBA_OK = 0
+RBA_ERR_NULL = -1
+RBA_ERR_SHAPE = -2
+RBA_ERR_UNSUPPORTED = -3
+RBA_ERR_WORKSPACE = -4
+RBA_ERR_HIP = -5
+BLOCK_SIZE = 128
+
+_i32 = ctypes.c_int32
+_ptr = ctypes.c_void_p
+_size = ctypes.c_size_t
+
+
+class AttnParams(ctypes.Structure):
+    """Mirror of rba_attn_params in include/rba.h."""
+    _fields_ = [
+        ("num_heads_q", _i32),
+        ("num_heads_kv", _i32),
+        ("head_dim_qk", _i32),
+        ("head_dim_v", _i32),
+        ("rel_extent", _i32),
+        ("window", _i32),
+        ("scale", ctypes.c_float),
+        ("block_size", _i32),
+    ]
+
+
+class RbaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"librba error {code}: {msg}")
+        self.code = code
+
+
+# (name, restype, argtypes) of every symbol include/rba.h declares
+_SIGNATURES = {
+    "rba_version": (ctypes.c_char_p, []),
+    "rba_last_error": (ctypes.c_char_p, []),
+    "rba_prefill": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                   _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr]),
+    "rba_validate_prefill": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr,
+                                            _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr]),
+    "rba_decode": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr, _i32,
+                                  _i32, _i32, _i32, _i32, _ptr, _size, _ptr, _ptr, _ptr]),
+    "rba_validate_decode": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr,
+                                           _ptr, _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
+    "rba_decode_plan_splits": (_i32, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _i32]),
+    "rba_decode_workspace_size": (_size, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _i32]),
+    "rba_decode_split": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                        _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
+    "rba_decode_combine": (ctypes.c_int, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _ptr, _size, _ptr,
+                                          _ptr, _ptr]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librba.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def version() -> str:
+    return lib().rba_version().decode()
+
+
+def last_error() -> str:
+    return lib().rba_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != RBA_OK:
+        raise RbaError(rc, last_error())
+
+
+def params(num_heads_q: int, num_heads_kv: int, head_dim_v: int, rel_extent: int, window: int,
+           scale: float, head_dim_qk: int = 128, block_size: int = BLOCK_SIZE) -> AttnParams:
+    return AttnParams(num_heads_q, num_heads_kv, head_dim_qk, head_dim_v, rel_extent, window, scale,
+                      block_size)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: int, scale: float,
+            max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rba_prefill. q [total_q, Hq, 128] bf16; k_cache [nb, Hkv, 128, 128] bf16;
+    v_cache [nb, Hkv, 128, dv] bf16; rel [total_q, Hq, R] fp32; cu_q [B+1],
+    seq_lens [B], block_tables [B, max_blocks] int32. max_q_len / max_seq_len
+    are host-side bounds (no device read happens here)."""
+    total_q, Hq, dqk = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    R = rel.shape[2]
+    if rel.shape[:2] != (total_q, Hq):
+        raise ValueError("rel must be [total_q, Hq, R]")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be 2-D")
+    batch = cu_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, Hq, dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
+    _check(lib().rba_prefill(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+        _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
+        int(max_seq_len), _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+    return out, lse
+
+
+def plan_splits(Hq, Hkv, dv, rel_extent, window, scale, batch, n_q, max_seq_len, num_cus=256) -> int:
+    p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    n = lib().rba_decode_plan_splits(ctypes.byref(p), batch, n_q, max_seq_len, num_cus)
+    if n < 1:
+        raise RbaError(n, last_error())
+    return n
+
+
+def workspace_size(Hq, Hkv, dv, rel_extent, window, scale, batch, n_q, max_seq_len, num_splits=0) -> int:
+    p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    return lib().rba_decode_workspace_size(ctypes.byref(p), batch, n_q, max_seq_len, num_splits)
+
+
+def _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q, window, scale):
+    rows, Hq, dqk = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    R = rel.shape[2]
+    if rows % n_q != 0:
+        raise ValueError("q rows must be batch * n_q")
+    if rel.shape[:2] != (rows, Hq):
+        raise ValueError("rel must be [batch * n_q, Hq, R]")
+    batch = rows // n_q
+    if seq_lens.numel() != batch:
+        raise ValueError("seq_lens must have batch entries")
+    return params(Hq, Hkv, dv, R, window, scale, dqk, bs), batch, rows, Hq, dv, nb
+
+
+def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
+           max_seq_len: int, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           want_lse: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rba_decode (split-KV + combine). q [batch*n_q, Hq, 128] bf16; rel
+    [batch*n_q, Hq, R] fp32. `workspace` (uint8, on the GPU) is allocated with
+    torch if not given."""
+    p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
+                                                window, scale)
+    L = lib()
+    need = L.rba_decode_workspace_size(ctypes.byref(p), batch, n_q, int(max_seq_len), int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    _check(L.rba_decode(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+    return out, lse
+
+
+def decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
+                 max_seq_len: int, num_splits: int, workspace: torch.Tensor, stream=None) -> None:
+    """rba_decode_split: partial outputs of every split into `workspace`."""
+    p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
+                                                window, scale)
+    _check(lib().rba_decode_split(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, scale: float, batch: int,
+                   n_q: int, num_splits: int, workspace: torch.Tensor, out: torch.Tensor,
+                   lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """rba_decode_combine: log-sum-exp merge of the partials in `workspace`."""
+    p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    _check(lib().rba_decode_combine(
+        ctypes.byref(p), batch, n_q, int(num_splits), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))

@@ -1,0 +1,105 @@
+"""Test/bench glue: run the library on a workloads.Batch and run the oracle on
+the same inputs. Test infrastructure (it imports the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from relative_position_bias_amd import rba
+
+TOL_MAX = 1.5e-2   # max |gpu - oracle| over every compared element
+TOL_MEAN = 2e-3    # mean |gpu - oracle|
+
+
+def oracle_batch(batch: workloads.Batch, rows=None):
+    """Float64 oracle on a CPU Batch, one sequence at a time (paging undone by
+    a plain gather of that sequence's blocks). rows: optional global rows; a
+    sampled row at position i is computed as the last query of the sequence's
+    first i+1 keys, which is the same result since later keys are invisible."""
+    total = batch.rows
+    out = np.full((total, batch.Hq, batch.dv), np.nan)
+    lse = np.full((total, batch.Hq), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    kw = dict(rel_extent=batch.R, window=batch.W, scale=batch.scale)
+    start = 0
+    for b, ql in enumerate(batch.q_lens):
+        L = int(batch.seq_lens[b])
+        local = None
+        if want is not None:
+            local = [r - start for r in range(start, start + ql) if r in want]
+            if not local:
+                start += ql
+                continue
+        nb = (L + workloads.BLOCK - 1) // workloads.BLOCK
+        blocks = batch.block_tables[b, :nb].long()
+        k = oracle.unpage(batch.k_cache[blocks].double().numpy(), [list(range(nb))], [L])
+        v = oracle.unpage(batch.v_cache[blocks].double().numpy(), [list(range(nb))], [L])
+        if local is None:
+            o, l = oracle.attend(batch.q[start:start + ql].double().numpy(), k, v,
+                                 batch.rel[start:start + ql].double().numpy(), [ql], [L], **kw)
+            out[start:start + ql] = o
+            lse[start:start + ql] = l
+        else:
+            for r in local:
+                i = L - ql + r
+                t = start + r
+                o, l = oracle.attend(batch.q[t:t + 1].double().numpy(), k[:i + 1], v[:i + 1],
+                                     batch.rel[t:t + 1].double().numpy(), [1], [i + 1], **kw)
+                out[t] = o[0]
+                lse[t] = l[0]
+        start += ql
+    return out, lse
+
+
+def run_prefill(b: workloads.Batch, want_lse=False, **kw):
+    return rba.prefill(b.q, b.k_cache, b.v_cache, b.rel, b.cu_q, b.seq_lens, b.block_tables,
+                       window=b.W, scale=b.scale, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
+                       want_lse=want_lse, **kw)
+
+
+def run_decode(b: workloads.Batch, num_splits=0, want_lse=False, **kw):
+    return rba.decode(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
+                      window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
+                      want_lse=want_lse, **kw)
+
+
+def run(b: workloads.Batch, **kw):
+    return run_prefill(b, **kw) if b.kind == "prefill" else run_decode(b, **kw)
+
+
+def errors(gpu_out: torch.Tensor, ref: np.ndarray, rows=None):
+    g = gpu_out.detach().float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    if not np.isfinite(g).all():
+        return float("inf"), float("inf")
+    d = np.abs(g - ref)
+    return float(d.max()), float(d.mean())
+
+
+def assert_close(gpu_out, ref, rows=None, what=""):
+    mx, mean = errors(gpu_out, ref, rows)
+    assert mx <= TOL_MAX and mean <= TOL_MEAN, f"{what}: max {mx:.3e} mean {mean:.3e}"
+    return mx, mean
+
+
+def sample_rows(batch: workloads.Batch, per_edge=16, extra=16, seed=0):
+    """Rows the oracle computes one by one on large inputs: the first and last
+    rows of each sequence, rows whose distance to the first key crosses R or W,
+    and a seeded random sample."""
+    rng = np.random.default_rng(seed)
+    rows, start = set(), 0
+    for b, ql in enumerate(batch.q_lens):
+        L = int(batch.seq_lens[b])
+        ctx = L - ql
+        rows.update(range(start, start + min(per_edge, ql)))
+        rows.update(range(start + max(0, ql - per_edge), start + ql))
+        for edge in (batch.R, batch.W):
+            if edge and ctx < edge < L:
+                r0 = start + (edge - ctx)
+                rows.update(r for r in range(r0 - 4, r0 + 4) if start <= r < start + ql)
+        rows.update((start + rng.integers(0, ql, size=min(extra, ql))).tolist())
+        start += ql
+    return sorted(rows)

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar: max |gpu - oracle| <= 1.5e-2 and mean <= 2e-3 on bf16 inputs (fp32
+output), every output finite. Small cases are compared element by element on
+every row; the full-size workloads either fully (when the oracle finishes in
+seconds) or on sampled rows that always include each sequence's first and
+last rows and the rows around the distance R / W edges.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from harness import (assert_close, errors, oracle_batch, run, run_decode, run_prefill, sample_rows)
+from relative_position_bias_amd import rba
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_vs_oracle(b_cpu, rows=None, what="", **kw):
+    b = b_cpu.to(DEV)
+    out, lse = run(b, want_lse=True, **kw)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_batch(b_cpu, rows=rows)
+    mx, mean = assert_close(out, ref, rows, what)
+    lmx, _ = errors(lse, ref_lse, rows)
+    assert lmx <= 1e-3, f"{what}: lse max err {lmx:.3e}"
+    return out, mx, mean
+
+
+# ---------------------------------------------------------------------------
+# small prefill cases: several tiles, ragged tails, every row compared
+# ---------------------------------------------------------------------------
+PREFILL_GRID = [
+    # q_lens, ctx_lens, Hq, Hkv, dv, R, W
+    ([256], [0], 4, 1, 128, 128, 64),          # the tiny workload's shape
+    ([200, 77], [0, 300], 8, 2, 128, 64, 0),
+    ([130], [1000], 8, 2, 64, 128, 100),
+    ([1], [0], 4, 4, 128, 4, 0),               # one token, G = 1
+    ([300], [33], 16, 2, 128, 256, 0),         # G = 8
+    ([97, 5, 64], [31, 400, 0], 12, 2, 128, 40, 37),  # G = 6, odd window
+    ([64], [4096], 4, 1, 64, 1024, 0),         # chunk over a long context
+    ([333], [0], 2, 2, 128, 8, 1),             # window of 1: only the key itself
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_GRID, ids=lambda c: f"q{c[0]}ctx{c[1]}H{c[2]}/{c[3]}dv{c[4]}R{c[5]}W{c[6]}")
+def test_prefill_small(case):
+    q_lens, ctx, Hq, Hkv, dv, R, Wn = case
+    say(f"prefill small {case}")
+    b = W.make_prefill(11, q_lens, ctx, Hq, Hkv, dv, R, Wn)
+    gpu_vs_oracle(b, what=str(case))
+
+
+def test_tiny_prefill_workload():
+    say("tiny_prefill_256")
+    gpu_vs_oracle(W.build("tiny_prefill_256"), what="tiny")
+
+
+def test_local_prefill_8k_full():
+    say("local_prefill_8k (all rows)")
+    _, mx, mean = gpu_vs_oracle(W.build("local_prefill_8k"), what="local 8k")
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+def test_global_chunked_prefill_sampled():
+    name = "global_chunked_prefill_32k"
+    full = W.build(name)
+    full_gpu = full.to(DEV)
+    for c, (ch_cpu, ch) in enumerate(zip(W.chunks(name, full), W.chunks(name, full_gpu))):
+        say(f"chunk {c}")
+        out, _ = run_prefill(ch)
+        torch.cuda.synchronize()
+        rows = sample_rows(ch_cpu, per_edge=8, extra=8, seed=c)
+        ref, _ = oracle_batch(ch_cpu, rows=rows)
+        mx, mean = assert_close(out, ref, rows, f"chunk {c}")
+        say(f"  rows {len(rows)} max {mx:.3e} mean {mean:.3e}")
+        assert torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+DECODE_GRID = [
+    # batch, n_q, lens, Hq, Hkv, dv, R, W, pool
+    (3, 1, [129, 1000, 5000], 32, 8, 128, 1024, 0, None),
+    (2, 4, [700, 4096], 64, 8, 64, 1024, 0, None),
+    (4, 3, [3, 250, 520, 1300], 16, 4, 128, 256, 300, None),
+    (2, 8, [900, 2000], 48, 8, 128, 512, 0, None),      # G = 6, 48 columns: 2 column groups
+    (5, 2, [128, 256, 384, 4000, 77], 8, 8, 64, 64, 128, 64),   # G = 1, aliased pool
+]
+
+
+@pytest.mark.parametrize("case", DECODE_GRID, ids=lambda c: f"B{c[0]}nq{c[1]}H{c[3]}/{c[4]}dv{c[5]}W{c[7]}")
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_decode_small(case, splits):
+    batch, n_q, lens, Hq, Hkv, dv, R, Wn, pool = case
+    say(f"decode small {case} splits={splits}")
+    b = W.make_decode(21, batch, n_q, Hq, Hkv, dv, R, Wn, seq_lens=lens, pool_blocks=pool)
+    gpu_vs_oracle(b, what=f"{case} s{splits}", num_splits=splits)
+
+
+def test_paged_decode_16_workload():
+    say("paged_decode_16x8k_128k (aliased 2560-block pool)")
+    _, mx, mean = gpu_vs_oracle(W.build("paged_decode_16x8k_128k"), what="decode16")
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+def test_paged_decode_16_disjoint_workload():
+    say("paged_decode_16x8k_128k_disjoint")
+    _, mx, mean = gpu_vs_oracle(W.build("paged_decode_16x8k_128k_disjoint"), what="decode16 disjoint")
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+@pytest.mark.parametrize("name", ["verify_decode_b1_100k", "verify_decode_b8_100k"])
+def test_verify_decode_workloads(name):
+    say(name)
+    _, mx, mean = gpu_vs_oracle(W.build(name), what=name)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+def test_split_count_invariance():
+    say("split invariance")
+    b = W.make_decode(5, 2, 2, 32, 8, 128, 1024, 0, seq_lens=[3000, 7000]).to(DEV)
+    outs = []
+    for s in (1, 2, 0, 55):
+        o, l = run_decode(b, num_splits=s, want_lse=True)
+        outs.append((o.clone(), l.clone()))
+    for o, l in outs[1:]:
+        assert torch.allclose(o, outs[0][0], rtol=0, atol=1e-5)
+        assert torch.allclose(l, outs[0][1], rtol=0, atol=1e-5)
+
+
+def test_block_permutation_is_bitwise_invariant():
+    say("block permutation")
+    b = W.make_prefill(3, [300, 90], [100, 700], 8, 2, 128, 128, 0, extra_blocks=5)
+    o1, _ = run_prefill(b.to(DEV))
+    perm = torch.randperm(b.k_cache.shape[0], generator=torch.Generator().manual_seed(9))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel())
+    b2 = W.Batch(**{**b.__dict__})
+    b2.k_cache = b.k_cache[perm].contiguous()
+    b2.v_cache = b.v_cache[perm].contiguous()
+    t = b.block_tables.clone().long()
+    b2.block_tables = torch.where(t >= 0, inv[t.clamp(min=0)], t).to(torch.int32)
+    o2, _ = run_prefill(b2.to(DEV))
+    assert torch.equal(o1, o2)
+
+
+def test_window_blocks_outside_are_never_read():
+    """Blocks wholly outside every query's window: table entry -1 or NaN
+    poison leave the output bitwise unchanged (the local-window equivalence)."""
+    say("window skipping")
+    Wn = 200
+    b = W.make_prefill(4, [150], [1500], 8, 2, 128, 128, Wn)
+    o1, _ = run_prefill(b.to(DEV))
+    first_needed = (1500 - Wn + 1) // 128
+    b2 = W.Batch(**{**b.__dict__})
+    b2.block_tables = b.block_tables.clone()
+    b2.k_cache = b.k_cache.clone()
+    b2.v_cache = b.v_cache.clone()
+    for n in range(first_needed):
+        blk = int(b.block_tables[0, n])
+        b2.k_cache.view(torch.int16)[blk] = W.BF16_NAN
+        b2.v_cache.view(torch.int16)[blk] = W.BF16_NAN
+    o2, _ = run_prefill(b2.to(DEV))
+    b2.block_tables[0, :first_needed] = -1
+    o3, _ = run_prefill(b2.to(DEV))
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_chunked_prefill_is_bitwise_equal_to_one_shot():
+    say("chunking")
+    full = W.make_prefill(6, [512], [0], 8, 2, 128, 256, 0).to(DEV)
+    o_full, _ = run_prefill(full)
+    parts = [run_prefill(W.chunk_of(full, c, 128))[0] for c in range(4)]
+    assert torch.equal(torch.cat(parts), o_full)
+
+
+def test_decode_rows_match_prefill_rows():
+    say("decode vs prefill rows")
+    full = W.make_prefill(8, [600], [0], 16, 4, 128, 256, 0)
+    o_pre, _ = run_prefill(full.to(DEV))
+    n_q = 3
+    dec = W.Batch(kind="decode", Hq=16, Hkv=4, dv=128, R=256, W=0, scale=full.scale,
+                  q=full.q[-n_q:].contiguous(), k_cache=full.k_cache, v_cache=full.v_cache,
+                  rel=full.rel[-n_q:].contiguous(), seq_lens=full.seq_lens, block_tables=full.block_tables,
+                  n_q=n_q, q_lens=[n_q], max_q_len=n_q, max_seq_len=600)
+    o_dec, _ = run_decode(dec.to(DEV))
+    assert torch.allclose(o_dec, o_pre[-n_q:], rtol=0, atol=2e-3)
+
+
+def test_shear_probe_selects_exact_value_rows():
+    """q = k = 0 and a +40 bias at one visible distance per (row, head): the
+    output must be exactly that key's value row (every row's shear offset,
+    the GQA map and the paging checked at once)."""
+    say("shear probe")
+    b = W.make_prefill(12, [100, 37], [50, 222], 8, 2, 128, 96, 0)
+    b.q.zero_()
+    b.k_cache.zero_()
+    rel = torch.zeros_like(b.rel)
+    rng = np.random.default_rng(1)
+    expect = torch.empty((b.rows, 8, 128))
+    kv_tab = b.block_tables
+    t = 0
+    for s, (ql, L) in enumerate(zip(b.q_lens, b.seq_lens.tolist())):
+        for r in range(ql):
+            i = L - ql + r
+            for h in range(8):
+                d0 = int(rng.integers(0, min(i + 1, 96)))
+                rel[t, h, d0] = 40.0
+                j = i - d0
+                blk = int(kv_tab[s, j // 128])
+                expect[t, h] = b.v_cache[blk, h // 4, j % 128].float()
+            t += 1
+    b.rel = rel
+    out, _ = run_prefill(b.to(DEV))
+    assert torch.allclose(out.cpu(), expect, rtol=0, atol=1e-6)
+
+
+def test_repeatable_bitwise():
+    say("repeatability")
+    b = W.make_decode(2, 4, 2, 32, 8, 128, 1024, 0, seq_lens=[9000, 300, 1500, 4100]).to(DEV)
+    ref, _ = run_decode(b)
+    for _ in range(10):
+        o, _ = run_decode(b)
+        assert torch.equal(o, ref)
+    p = W.make_prefill(2, [500], [700], 8, 2, 128, 512, 300).to(DEV)
+    pref, _ = run_prefill(p)
+    for _ in range(10):
+        assert torch.equal(run_prefill(p)[0], pref)
+
+
+def test_graph_capture_replay():
+    say("graph capture")
+    b = W.make_decode(13, 2, 4, 64, 8, 64, 1024, 0, seq_lens=[2000, 5000]).to(DEV)
+    ws = torch.empty(rba.workspace_size(64, 8, 64, 1024, 0, b.scale, 2, 4, 5000), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty((8, 64, 64), device=DEV)
+    eager, _ = run_decode(b, workspace=ws)
+    eager = eager.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_decode(b, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_decode(b, workspace=ws, out=out)
+    for _ in range(3):
+        out.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        run_prefill(W.make_prefill(1, [64], [0], 4, 1, 128, 128, 0).to(DEV))   # eager work between
+
+
+def test_invalid_block_id_gives_nan_not_a_fault():
+    say("invalid block id")
+    b = W.make_decode(3, 2, 1, 8, 2, 128, 64, 0, seq_lens=[500, 600])
+    b.block_tables[1, 2] = 10_000          # out of range for this pool
+    out, _ = run_decode(b.to(DEV))
+    out = out.cpu()
+    assert torch.isnan(out[1]).all()
+    assert torch.isfinite(out[0]).all()
