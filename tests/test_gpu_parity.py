@@ -132,15 +132,21 @@ def test_verify_decode_workloads(name):
 # invariants on the GPU
 # ---------------------------------------------------------------------------
 def test_split_count_invariance():
+    """Different split counts agree: lse (built from fp32 sums) to fp32
+    rounding; out to the bf16 rounding of P, which is taken relative to each
+    split's own reference max (relative error <= 2^-9 per weight, so at most
+    ~2^-8 * max|v| in the worst case and far less on average)."""
     say("split invariance")
     b = W.make_decode(5, 2, 2, 32, 8, 128, 1024, 0, seq_lens=[3000, 7000]).to(DEV)
     outs = []
     for s in (1, 2, 0, 55):
         o, l = run_decode(b, num_splits=s, want_lse=True)
         outs.append((o.clone(), l.clone()))
+    vmax = float(b.v_cache.float().nan_to_num(0).abs().max())
     for o, l in outs[1:]:
-        assert torch.allclose(o, outs[0][0], rtol=0, atol=1e-5)
-        assert torch.allclose(l, outs[0][1], rtol=0, atol=1e-5)
+        d = (o - outs[0][0]).abs()
+        assert float(d.max()) <= 2.0 ** -8 * vmax and float(d.mean()) <= 2e-4
+        assert torch.allclose(l, outs[0][1], rtol=0, atol=2e-5)
 
 
 def test_block_permutation_is_bitwise_invariant():
