@@ -140,6 +140,49 @@ def _sampled_prefill_work(b, rows):
     return flops, nbytes
 
 
+def workload_report(name, steps, warmup, dev):
+    """Per-call times of one named workload (each call timed with events on
+    its stream), with algorithmic TFLOP/s, GB/s and roofline fractions."""
+    import torch
+
+    import workloads as W
+    from harness import run_decode, run_prefill
+
+    full = W.build(name)
+    gpu = full.to(dev)
+    if W.WORKLOADS[name]["kind"] == "chunked":
+        calls = list(zip(W.chunks(name, full), W.chunks(name, gpu)))
+    else:
+        calls = [(full, gpu)]
+    stream = torch.cuda.current_stream()
+    res = []
+    for b_cpu, b in calls:
+        fn = (lambda b=b: run_prefill(b)) if b.kind == "prefill" else (lambda b=b: run_decode(b))
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b2) for a, b2 in ev)
+        f, nbytes, _ = algorithmic(b_cpu, b.kind)
+        t = ms[len(ms) // 2] / 1e3
+        res.append({"ms_median": round(ms[len(ms) // 2], 4), "ms_min": round(ms[0], 4),
+                    "tflops": round(f / t / 1e12, 2), "gbps": round(nbytes / t / 1e9, 1),
+                    "frac_mfma": round(f / t / PEAK_MFMA_BF16, 4), "frac_hbm": round(nbytes / t / PEAK_HBM, 4),
+                    "roof_ms": round(roof_time(f, nbytes) * 1e3, 4), "flops": f, "bytes": nbytes})
+    tot = sum(r["ms_median"] for r in res)
+    roof = sum(r["roof_ms"] for r in res)
+    print(json.dumps({"workload": name, "calls": res, "total_ms": round(tot, 4),
+                      "roofline_frac": round(roof / tot, 4),
+                      "tflops_total": round(sum(r["flops"] for r in res) / tot / 1e9, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", default=None,
+                    help="time one named workload on its own (a report line, not the step line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +208,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload:
+        workload_report(args.workload, args.steps, args.warmup, dev)
+        return
     t_gen = time.perf_counter()
     pre_cpu = W.build(PREFILL)
     dec_cpu = W.build(DECODE)

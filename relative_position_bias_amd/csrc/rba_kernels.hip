@@ -17,25 +17,32 @@
 //     probabilities are already in the B-operand layout of the P.V MFMA.
 //   * The K rows fed to the MFMA A operand are permuted (bits 2 and 3 of the
 //     row index swapped) so that every lane ends up with 8 CONSECUTIVE keys per
-//     16-key chunk: the P.V A operand (V transposed in LDS) is then one 16-byte
-//     LDS read, and the lane's bias values are contiguous in the rel row.
+//     16-key chunk: the lane's bias values are then contiguous in its rel row,
+//     and the P.V A operand is 8 consecutive keys of one value dimension.
+//   * V stays in LDS in its natural [key][dim] layout and is read transposed
+//     with ds_read_b64_tr_b16 (gfx950): two reads give a lane the 8 keys of
+//     one value dimension that the P.V MFMA needs. No shuffles, no transposed
+//     writes.
 //   * The bias is "sheared": element (column n, key j) needs rel[t_n, h_n,
-//     i_n - j]. Each wave stages, per subtile, the aligned superset of its 32
-//     rel row segments (32 rows x 36 floats) into LDS with 16-byte loads, then
-//     every lane reads its own 16 values along the shear from LDS. Subtiles
-//     whose distances are all >= R skip the rel traffic entirely; subtiles
+//     i_n - j]. Per 32-key subtile each wave loads, with 16-byte loads, the
+//     aligned superset of its 32 rel row segments (32 rows x 36 floats), parks
+//     it in its own LDS band and reads every lane's 16 values back along the
+//     shear. Subtiles whose distances are all >= R skip rel entirely; subtiles
 //     that are entirely masked (causal / window) are skipped.
-//   * K and V blocks (128 keys) are staged once per workgroup in LDS; V is
-//     transposed on the way in (v_perm) so keys are contiguous per value dim.
 //   * Online softmax in fp32 in the log2 domain with a lazy reference: the
-//     reference max moves only when a block's max exceeds it by > 8 (exact
+//     reference max moves only when a subtile's max exceeds it by > 8 (exact
 //     rearrangement; p <= 2^8), so the rescale of the accumulator is rare.
-//   * Prefill: a workgroup of 8 waves shares one K/V block for up to 8 query
-//     heads of one KV head (GQA packing) and 32..256 query rows.
-//   * Decode: a workgroup of 4 waves shares each K/V block; wave w takes
-//     subtile w, so each block is read from HBM once for all G * n_q columns;
-//     splits of the block range go to different workgroups and a small
-//     kernel merges them by log-sum-exp.
+//   * Prefill: a workgroup of 8 waves shares each 128-key K/V block in LDS for
+//     up to 8 query heads of one KV head (GQA packing) and 32..256 query rows.
+//     The next block's K/V and the next subtile's rel are prefetched into
+//     registers while the current one is computed; the block-table slice sits
+//     in a register (one entry per lane) so no load waits on a table read.
+//   * Decode: each of the 4 waves of a workgroup streams its own 32-key
+//     subtile of every block of the split without any barrier: K goes straight
+//     from HBM into MFMA operand registers, V into a wave-private LDS tile.
+//     Each block is read once for all G * n_q columns; splits of the block
+//     range go to different workgroups and a small kernel merges them by
+//     log-sum-exp.
 //   * Work-unit order puts the KV head in the fastest position of blockIdx so
 //     that, with workgroups dealt round-robin to the 8 XCDs, all workgroups of
 //     one KV head (which share its K/V) land on the same XCD and its L2.
@@ -52,16 +59,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BS = 128;        // keys per cache block
 constexpr int DQK = 128;       // query/key head size
 constexpr int KROW = DQK + 8;  // bf16 per LDS row of K (16-byte pad)
-constexpr int VROW = BS + 8;   // bf16 per LDS row of transposed V
 constexpr int RROW = 40;       // floats per LDS row of a staged rel band (36 used)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float TAU = 8.0f;    // lazy-rescale threshold, log2 units
+
+// bf16 per LDS row of V in its natural layout; the 32-byte pad puts the 4
+// rows one transposed read touches on distinct banks.
+template <int DV>
+constexpr int vrow() { return DV + 16; }
 
 __device__ __forceinline__ int perm32(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -80,52 +92,23 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
-// Stage one K block (128 keys x 128 dims, bf16) into LDS with the row
-// permutation the transposed-score MFMA expects: key r goes to LDS row
-// (r & ~31) | perm32(r & 31).
-template <int NT>
-__device__ __forceinline__ void stage_k(__bf16* Ks, const uint16_t* kblk, int tid) {
-#pragma unroll
-    for (int it = 0; it < (BS * DQK / 8) / NT; ++it) {
-        const int p = tid + NT * it;
-        const int row = p >> 4, c16 = p & 15;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(kblk + row * DQK + c16 * 8);
-        const int lrow = (row & ~31) | perm32(row & 31);
-        *reinterpret_cast<u32x4*>(Ks + lrow * KROW + c16 * 8) = val;
-    }
-}
-
-// Stage one V block (128 keys x DV, bf16) into LDS transposed: Vt[dv][key].
-// Keys at or past `nvalid` (beyond the sequence) are written as zeros so that
-// whatever the cache holds there contributes exactly 0.
-template <int DV, int NT>
-__device__ __forceinline__ void stage_v(__bf16* Vt, const uint16_t* vblk, int nvalid, int tid) {
-    constexpr int UNITS = 32 * (DV / 8);  // units of 4 keys x 8 value dims
-#pragma unroll
-    for (int u0 = 0; u0 < UNITS; u0 += NT) {
-        const int u = u0 + tid;
-        if (UNITS % NT != 0 && u >= UNITS) break;
-        const int c = u % (DV / 8), kg = u / (DV / 8);
-        u32x4 in[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = 4 * kg + r;
-            if (key < nvalid) {
-                in[r] = *reinterpret_cast<const u32x4*>(vblk + key * DV + 8 * c);
-            } else {
-                in[r] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            const int qd = j >> 1;
-            u32x2 o;
-            o[0] = __builtin_amdgcn_perm(in[1][qd], in[0][qd], sel);
-            o[1] = __builtin_amdgcn_perm(in[3][qd], in[2][qd], sel);
-            *reinterpret_cast<u32x2*>(Vt + (8 * c + j) * VROW + 4 * kg) = o;
-        }
-    }
+// P.V A operand from V in natural layout [key][dim] (row stride `vs` bf16):
+// lane gets V[key0 + 8 (lane>>5) + 0..7][dv0 + (lane & 31)] as 8 bf16, via two
+// transposed LDS reads. ds_read_b64_tr_b16 hands lane i of each 16-lane group
+// the (i % 4)-th 16-bit element at the address given by lane 4k + i/4, for
+// k = 0..3; the addresses below make that element V[row k][dv0 + lane & 31].
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* Vs, int vs, int key0, int dv0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const __bf16* p = Vs + (key0 + 8 * (g >> 1) + (j >> 2)) * vs + dv0 + 16 * (g & 1) + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * vs));
+    union {
+        s16x4 h[2];
+        bf16x8 v;
+    } u;
+    u.h[0] = lo;
+    u.h[1] = hi;
+    return u.v;
 }
 
 // Per-wave state of 32 attention columns (one per lane & 31).
@@ -141,67 +124,88 @@ struct Cols {
     bool m_set;
 };
 
-// Stage the rel values one 32-key subtile needs (rows = the wave's columns)
-// into this wave's LDS band: row n holds rel[t_n, h_n, a_n .. a_n + 36) with
-// a_n = floor4(pos_n - js - 31). Each lane loads float4 pieces of its own row;
-// pieces outside [0, R) are zeros (distance >= R has bias 0, distance < 0 is
-// masked anyway).
-__device__ __forceinline__ void stage_rel(float* Rw, const float* relrow, int pos, int js, int R,
-                                          int lane) {
-    const int n = lane & 31, hh = lane >> 5;
+template <int DV>
+__device__ __forceinline__ bool masked_all(const Cols<DV>& C, int js, int W) {
+    return js > C.w_hi || (W > 0 && C.w_lo - (js + 31) >= W);
+}
+
+template <int DV>
+__device__ __forceinline__ bool bias_on(const Cols<DV>& C, int js, int R) {
+    return C.w_lo - (js + 31) < R;
+}
+
+// rel pieces one 32-key subtile needs for this lane's own row: row n needs
+// rel[t_n, h_n, a_n .. a_n + 36) with a_n = floor4(pos_n - js - 31); lane
+// (n, hh) holds the float4 pieces c4 = hh, hh + 2, ... < 9. Pieces outside
+// [0, R) are zeros (distance >= R has bias 0, distance < 0 is masked).
+struct RelRegs {
+    f32x4 r[5];
+};
+
+__device__ __forceinline__ void rel_load(RelRegs& v, const float* relrow, int pos, int js, int R, int lane) {
+    const int hh = lane >> 5;
     const int a_n = (pos - js - 31) & ~3;
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
         const int c4 = hh + 2 * k;
-        if (c4 < 9) {
-            const int a = a_n + 4 * c4;
-            f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (pos >= 0 && a >= 0 && a + 4 <= R) val = *reinterpret_cast<const f32x4*>(relrow + a);
-            *reinterpret_cast<f32x4*>(Rw + n * RROW + 4 * c4) = val;
-        }
+        const int a = a_n + 4 * c4;
+        v.r[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c4 < 9 && pos >= 0 && a >= 0 && a + 4 <= R) v.r[k] = *reinterpret_cast<const f32x4*>(relrow + a);
     }
 }
 
-// One 32-key subtile starting at key js against the wave's 32 columns:
-// QK^T on MFMA, bias along the shear, masks, online softmax, P.V on MFMA.
-// `Ksub` points at the subtile's first LDS row of K, `Vsub` at its first key
-// column of the transposed V.
-template <int DV>
-__device__ __forceinline__ void subtile(Cols<DV>& C, const __bf16* Ksub, const __bf16* Vsub,
-                                        float* Rw, int js, int R, int W, float c1, int lane) {
+__device__ __forceinline__ void rel_store(float* Rw, const RelRegs& v, int lane) {
     const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const int c4 = hh + 2 * k;
+        if (c4 < 9) *reinterpret_cast<f32x4*>(Rw + n * RROW + 4 * c4) = v.r[k];
+    }
+}
 
-    // S^T = K_sub . Q^T
+// Start of this lane's bias values in its staged LDS row: bias for register r
+// (key js + 16 (r/8) + 8 hh + r%8) is rb[16 (1 - r/8) + 7 - r%8].
+__device__ __forceinline__ const float* rel_row_ptr(const float* Rw, int pos, int lane) {
+    const int n = lane & 31, hh = lane >> 5;
+    return Rw + n * RROW + (8 + ((pos + 1) & 3) - 8 * hh);
+}
+
+// S^T for one 32-key subtile whose K rows sit in LDS (row m holds key perm32(m)).
+__device__ __forceinline__ f32x16 qk_lds(const __bf16* Ksub, const bf16x8 (&qreg)[8], int lane) {
     f32x16 s = zero16();
-    {
-        const __bf16* krow = Ksub + n * KROW + 8 * hh;
+    const __bf16* krow = Ksub + (lane & 31) * KROW + 8 * (lane >> 5);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * st);
-            s = mfma32(a, C.qreg[st], s);
-        }
+    for (int st = 0; st < 8; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * st);
+        s = mfma32(a, qreg[st], s);
     }
+    return s;
+}
 
-    // lane holds keys js + 16 (r/8) + 8 hh + r%8 of column n
-    const bool bias_on = (C.w_lo - (js + 31)) < R;
+// S^T for one 32-key subtile whose K operand is already in registers.
+__device__ __forceinline__ f32x16 qk_regs(const bf16x8 (&kreg)[8], const bf16x8 (&qreg)[8]) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) s = mfma32(kreg[st], qreg[st], s);
+    return s;
+}
+
+// Bias, masks, online softmax and P.V for one 32-key subtile starting at key
+// js. `s` holds S^T (lane: keys js + 16 (r/8) + 8 (lane>>5) + r%8 of column
+// lane & 31); `rb` is the lane's staged bias row (rel_row_ptr) or null when no
+// distance of the subtile is below R. `vread(dt, c)` returns the P.V A
+// operand: V^T rows 32 dt + (lane & 31), keys 16 c + 8 (lane>>5) .. +8.
+template <int DV, class VRead>
+__device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, const float* rb, int js, int W,
+                                           float c1, int lane, VRead vread) {
+    const int hh = lane >> 5;
     const bool need_mask = C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W);
-
-    float bias[16];
-    if (bias_on) {
-        stage_rel(Rw, C.relrow, C.pos, js, R, lane);
-        __builtin_amdgcn_wave_barrier();
-        const int delta = (C.pos + 1) & 3;
-        const float* rb = Rw + n * RROW + (8 + delta - 8 * hh);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bias[r] = rb[16 * (1 - (r >> 3)) + 7 - (r & 7)];
-        __builtin_amdgcn_wave_barrier();
-    }
 
     float x[16];
     float M = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const float bterm = bias_on ? fmaf(bias[r], LOG2E, -C.m_ref) : -C.m_ref;
+        const float bterm = rb ? fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], LOG2E, -C.m_ref) : -C.m_ref;
         float t = fmaf(s[r], c1, bterm);
         if (need_mask) {
             const int key = js + 16 * (r >> 3) + 8 * hh + (r & 7);
@@ -236,11 +240,7 @@ __device__ __forceinline__ void subtile(Cols<DV>& C, const __bf16* Ksub, const _
             pb[i] = (__bf16)p;
         }
 #pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt) {
-            const bf16x8 va =
-                *reinterpret_cast<const bf16x8*>(Vsub + (32 * dt + n) * VROW + 16 * c + 8 * hh);
-            C.O[dt] = mfma32(va, pb, C.O[dt]);
-        }
+        for (int dt = 0; dt < DV / 32; ++dt) C.O[dt] = mfma32(vread(dt, c), pb, C.O[dt]);
     }
 }
 
@@ -267,13 +267,73 @@ __device__ __forceinline__ void init_acc(Cols<DV>& C) {
     C.m_set = false;
 }
 
+// Write the normalised output (and lse) of a finished wave: lane holds
+// dv = 32 dt + 8 q4 + 4 hh + k of column lane & 31.
+template <int DV>
+__device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float* lse, bool bad, int lane) {
+    const float l_tot = C.l_sum + xor32(C.l_sum);
+    const float inv = bad ? NAN : 1.f / l_tot;
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = C.O[dt][4 * q4 + k] * inv;
+            *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * q4 + 4 * hh) = o;
+        }
+    }
+    if (lse != nullptr && hh == 0) *lse = bad ? NAN : (C.m_ref + __log2f(l_tot)) * LN2;
+}
+
 // ---------------------------------------------------------------------------
 // Prefill
 // ---------------------------------------------------------------------------
+
+// One 128-key K/V block held in registers (prefetch) by a 512-thread workgroup.
+template <int DV>
+struct KVRegs {
+    u32x4 k[4];
+    u32x4 v[DV / 32];
+};
+
+template <int DV>
+__device__ __forceinline__ void kv_load(KVRegs<DV>& r, const uint16_t* kblk, const uint16_t* vblk, int nvalid,
+                                        int tid) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int p = tid + 512 * it;
+        r.k[it] = *reinterpret_cast<const u32x4*>(kblk + (p >> 4) * DQK + 8 * (p & 15));
+    }
+#pragma unroll
+    for (int it = 0; it < DV / 32; ++it) {
+        const int p = tid + 512 * it;
+        const int key = p / (DV / 8), c = p % (DV / 8);
+        r.v[it] = key < nvalid ? *reinterpret_cast<const u32x4*>(vblk + key * DV + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// K rows go to LDS row (r & ~31) | perm32(r & 31); V rows keep their order.
+template <int DV>
+__device__ __forceinline__ void kv_store(__bf16* Ks, __bf16* Vs, const KVRegs<DV>& r, int tid) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int p = tid + 512 * it;
+        const int row = p >> 4;
+        *reinterpret_cast<u32x4*>(Ks + ((row & ~31) | perm32(row & 31)) * KROW + 8 * (p & 15)) = r.k[it];
+    }
+#pragma unroll
+    for (int it = 0; it < DV / 32; ++it) {
+        const int p = tid + 512 * it;
+        *reinterpret_cast<u32x4*>(Vs + (p / (DV / 8)) * vrow<DV>() + 8 * (p % (DV / 8))) = r.v[it];
+    }
+}
+
 template <int DV>
 __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[BS * KROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[DV * VROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[BS * vrow<DV>()];
     __shared__ __attribute__((aligned(16))) float Rs[8 * 32 * RROW];
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31;
@@ -314,58 +374,129 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
     const int kb_hi = i_hi / BS;
+    const int js_end = kb_hi * BS + 3 * 32;  // last subtile start
     float* Rw = Rs + wid * 32 * RROW;
+    const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
+    // block-table slice of the tile (lane i = entry tab_base + i)
+    int tab_base = kb_lo;
+    int tabv = (kb_lo + lane <= kb_hi) ? tab[kb_lo + lane] : -1;
+
+    auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
+
+    // rel for subtile js is loaded during subtile js - 32 and parked in LDS at
+    // the start of subtile js, just before the registers take the next load.
+    RelRegs rr;
+    if (rel_active(kb_lo * BS)) rel_load(rr, C.relrow, C.pos, kb_lo * BS, A.R, lane);
+
+    KVRegs<DV> kv;
+    int phys = __builtin_amdgcn_readlane(tabv, 0);
+    bool ok = phys >= 0 && phys < A.num_blocks;
+    if (ok) {
+        const size_t base = ((size_t)phys * A.Hkv + g) * BS;
+        kv_load<DV>(kv, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, tid);
+    }
+
     for (int kb = kb_lo; kb <= kb_hi; ++kb) {
-        const int phys = A.tables[(long long)b * A.max_blocks + kb];
-        const bool ok = phys >= 0 && phys < A.num_blocks;
-        bad = bad || !ok;
+        const bool ok_cur = ok;
+        bad = bad || !ok_cur;
         __syncthreads();
-        if (ok) {
-            const size_t base = ((size_t)phys * A.Hkv + g) * BS;
-            stage_k<512>(Ks, A.k + base * DQK, tid);
-            stage_v<DV, 512>(Vt, A.v + base * DV, L - kb * BS, tid);
+        if (ok_cur) kv_store<DV>(Ks, Vs, kv, tid);
+        __syncthreads();
+        if (kb < kb_hi) {  // prefetch the next block while this one is computed
+            if (kb + 1 - tab_base >= 64) {
+                tab_base += 64;
+                tabv = (tab_base + lane <= kb_hi) ? tab[tab_base + lane] : -1;
+            }
+            phys = __builtin_amdgcn_readlane(tabv, kb + 1 - tab_base);
+            ok = phys >= 0 && phys < A.num_blocks;
+            if (ok) {
+                const size_t base = ((size_t)phys * A.Hkv + g) * BS;
+                kv_load<DV>(kv, A.k + base * DQK, A.v + base * DV, L - (kb + 1) * BS, tid);
+            }
         }
-        __syncthreads();
-        if (!ok || !wave_active) continue;
+        if (!wave_active) continue;
 #pragma unroll 1
         for (int sub = 0; sub < 4; ++sub) {
             const int js = kb * BS + 32 * sub;
-            const bool masked_all = js > C.w_hi || (A.W > 0 && C.w_lo - (js + 31) >= A.W);
-            if (masked_all) continue;
-            subtile<DV>(C, Ks + 32 * sub * KROW, Vt + 32 * sub, Rw, js, A.R, A.W, A.c1, lane);
+            const bool cur_rel = rel_active(js);
+            if (cur_rel) rel_store(Rw, rr, lane);
+            if (js + 32 <= js_end && rel_active(js + 32)) rel_load(rr, C.relrow, C.pos, js + 32, A.R, lane);
+            if (ok_cur && !masked_all(C, js, A.W)) {
+                const f32x16 s = qk_lds(Ks + 32 * sub * KROW, C.qreg, lane);
+                __builtin_amdgcn_wave_barrier();
+                const float* rb = cur_rel ? rel_row_ptr(Rw, C.pos, lane) : nullptr;
+                softmax_pv<DV>(C, s, rb, js, A.W, A.c1, lane, [&](int dt, int c) {
+                    return v_operand(Vs, vrow<DV>(), 32 * sub + 16 * c, 32 * dt, lane);
+                });
+            }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 
     if (!wave_active || !real) return;
-    const float l_tot = C.l_sum + xor32(C.l_sum);
-    const float inv = bad ? NAN : 1.f / l_tot;
-    const int hh = lane >> 5;
-    float* orow = A.out + trow * DV;
-#pragma unroll
-    for (int dt = 0; dt < DV / 32; ++dt) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = C.O[dt][4 * q4 + k] * inv;
-            *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * q4 + 4 * hh) = o;
-        }
-    }
-    if (A.lse != nullptr && hh == 0) A.lse[trow] = bad ? NAN : (C.m_ref + __log2f(l_tot)) * LN2;
+    store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, lane);
 }
 
 // ---------------------------------------------------------------------------
 // Split-KV decode
+//
+// Each of the 4 waves streams subtile w (keys 32 w .. 32 w + 31) of every
+// block of its split, independently of the other waves (no barrier in the
+// main loop): K goes straight from HBM into the MFMA A-operand registers, V
+// into a wave-private LDS tile in natural layout. The split's block-table
+// slice is held in one register (lane i = entry i) and read with readlane, so
+// no block waits on a dependent table load. The four waves' partial softmax
+// states are merged through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int DV>
-__global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs A) {
-    // K and V staging; reused at the end for the cross-wave merge.
-    __shared__ __attribute__((aligned(16))) __bf16 KV[BS * KROW + DV * VROW];
-    __shared__ __attribute__((aligned(16))) float Rs[4 * 32 * RROW];
-    __bf16* Ks = KV;
-    __bf16* Vt = KV + BS * KROW;
+struct DecodeLds {
+    static constexpr int V_BYTES = 32 * vrow<DV>() * 2;
+    static constexpr int R_BYTES = 32 * RROW * 4;
+    static constexpr int WAVE = V_BYTES + R_BYTES;
+    static constexpr int MERGE = 4 * 32 * DV * 4 + 2 * 4 * 32 * 4;
+    static constexpr int TOTAL = (4 * WAVE > MERGE) ? 4 * WAVE : MERGE;
+};
+
+// K subtile (32 keys) of one block, in the MFMA A-operand layout: lane holds
+// key 32 sub + perm32(lane & 31), dims 16 st + 8 (lane >> 5) .. +8.
+__device__ __forceinline__ void load_k_sub(bf16x8 (&kr)[8], const uint16_t* kblk, int sub, int lane) {
+    const uint16_t* row = kblk + (32 * sub + perm32(lane & 31)) * DQK + 8 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kr[st] = *reinterpret_cast<const bf16x8*>(row + 16 * st);
+}
+
+// V subtile (32 keys x DV) as 16-byte pieces, lane takes pieces lane + 64 k;
+// keys at or past `nvalid` (beyond the sequence) are zeros.
+template <int DV>
+struct VSub {
+    static constexpr int PIECES = 32 * (DV / 8) / 64;  // per lane
+    u32x4 r[PIECES];
+};
+
+template <int DV>
+__device__ __forceinline__ void load_v_sub(VSub<DV>& v, const uint16_t* vblk, int sub, int nvalid, int lane) {
+#pragma unroll
+    for (int k = 0; k < VSub<DV>::PIECES; ++k) {
+        const int p = lane + 64 * k;
+        const int key = 32 * sub + p / (DV / 8), c = p % (DV / 8);
+        v.r[k] = key < nvalid ? *reinterpret_cast<const u32x4*>(vblk + key * DV + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int DV>
+__device__ __forceinline__ void store_v_sub(__bf16* Vw, const VSub<DV>& v, int lane) {
+#pragma unroll
+    for (int k = 0; k < VSub<DV>::PIECES; ++k) {
+        const int p = lane + 64 * k;
+        *reinterpret_cast<u32x4*>(Vw + (p / (DV / 8)) * vrow<DV>() + 8 * (p % (DV / 8))) = v.r[k];
+    }
+}
+
+template <int DV>
+__global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
+    __shared__ __attribute__((aligned(16))) char smem[DecodeLds<DV>::TOTAL];
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int id = blockIdx.x;
@@ -399,33 +530,53 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs A) {
     const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
     const int s_lo = kb_first + split * A.bps;
     const int s_hi = min(s_lo + A.bps, nb);
-    float* Rw = Rs + wid * 32 * RROW;
+    __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * DecodeLds<DV>::WAVE);
+    float* Rw = reinterpret_cast<float*>(smem + wid * DecodeLds<DV>::WAVE + DecodeLds<DV>::V_BYTES);
+    const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
+    int tab_base = s_lo;
+    int tabv = (s_lo + lane < s_hi) ? tab[s_lo + lane] : -1;
     for (int kb = s_lo; kb < s_hi; ++kb) {
-        const int phys = A.tables[(long long)b * A.max_blocks + kb];
-        const bool ok = phys >= 0 && phys < A.num_blocks;
-        bad = bad || !ok;
-        __syncthreads();
-        if (ok) {
-            const size_t base = ((size_t)phys * A.Hkv + g) * BS;
-            stage_k<256>(Ks, A.k + base * DQK, tid);
-            stage_v<DV, 256>(Vt, A.v + base * DV, L - kb * BS, tid);
+        if (kb - tab_base >= 64) {
+            tab_base += 64;
+            tabv = (tab_base + lane < s_hi) ? tab[tab_base + lane] : -1;
         }
-        __syncthreads();
-        if (!ok) continue;
         const int js = kb * BS + 32 * wid;
-        const bool masked_all = js > C.w_hi || (A.W > 0 && C.w_lo - (js + 31) >= A.W);
-        if (masked_all) continue;
-        subtile<DV>(C, Ks + 32 * wid * KROW, Vt + 32 * wid, Rw, js, A.R, A.W, A.c1, lane);
+        if (masked_all(C, js, A.W)) continue;
+        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        if (phys < 0 || phys >= A.num_blocks) {
+            bad = true;
+            continue;
+        }
+        const size_t base = ((size_t)phys * A.Hkv + g) * BS;
+        const bool brel = bias_on(C, js, A.R);
+        bf16x8 kr[8];
+        VSub<DV> vs;
+        load_k_sub(kr, A.k + base * DQK, wid, lane);
+        load_v_sub<DV>(vs, A.v + base * DV, wid, L - kb * BS, lane);
+        store_v_sub<DV>(Vw, vs, lane);
+        RelRegs rr;
+        if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
+        const f32x16 s = qk_regs(kr, C.qreg);
+        const float* rb = nullptr;
+        if (brel) {
+            rel_store(Rw, rr, lane);
+            rb = rel_row_ptr(Rw, C.pos, lane);
+        }
+        __builtin_amdgcn_wave_barrier();
+        softmax_pv<DV>(C, s, rb, js, A.W, A.c1, lane,
+                       [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
+        __builtin_amdgcn_wave_barrier();
     }
 
     // Merge the four waves' partial states through LDS.
     __syncthreads();
-    float* Om = reinterpret_cast<float*>(KV);   // [4][32][DV]
-    float* Mm = Rs;                             // [4][32] reference max (or -inf)
-    float* Lm = Rs + 4 * 32;                    // [4][32] row sums
+    float* Om = reinterpret_cast<float*>(smem);   // [4][32][DV]
+    float* Mm = Om + 4 * 32 * DV;                 // [4][32] reference max (or -inf)
+    float* Lm = Mm + 4 * 32;                      // [4][32] row sums
     const float l_tot = C.l_sum + xor32(C.l_sum);
+    const bool any_bad = __syncthreads_or(bad);
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt) {
 #pragma unroll
@@ -442,7 +593,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs A) {
     }
     __syncthreads();
 
-    // 32 columns x DV values over 256 threads
     for (int e = tid; e < 32 * DV; e += 256) {
         const int col = e / DV, dv = e % DV;
         const int cc = cg * 32 + col;
@@ -464,10 +614,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs A) {
         }
         const int ctt = cc / A.G, chl = cc % A.G;
         const long long prow = ((long long)(b * A.n_q + ctt) * A.Hq + (g * A.G + chl)) * A.splits + split;
-        const float o = bad ? NAN : (M > -INFINITY ? num / den : 0.f);
-        A.part_o[prow * DV + dv] = o;
+        A.part_o[prow * DV + dv] = any_bad ? NAN : (M > -INFINITY ? num / den : 0.f);
         if (dv == 0) {
-            A.part_lse[prow] = bad ? NAN : (M > -INFINITY ? (M + __log2f(den)) * LN2 : -INFINITY);
+            A.part_lse[prow] = any_bad ? NAN : (M > -INFINITY ? (M + __log2f(den)) * LN2 : -INFINITY);
         }
     }
 }
