@@ -124,14 +124,16 @@ struct Cols {
     bool m_set;
 };
 
+__device__ __forceinline__ bool uniform(bool v);
+
 template <int DV>
 __device__ __forceinline__ bool masked_all(const Cols<DV>& C, int js, int W) {
-    return js > C.w_hi || (W > 0 && C.w_lo - (js + 31) >= W);
+    return uniform(js > C.w_hi || (W > 0 && C.w_lo - (js + 31) >= W));
 }
 
 template <int DV>
 __device__ __forceinline__ bool bias_on(const Cols<DV>& C, int js, int R) {
-    return C.w_lo - (js + 31) < R;
+    return uniform(C.w_lo - (js + 31) < R);
 }
 
 // rel pieces one 32-key subtile needs for this lane's own row: row n needs
@@ -190,31 +192,42 @@ __device__ __forceinline__ f32x16 qk_regs(const bf16x8 (&kreg)[8], const bf16x8 
     return s;
 }
 
+// Wave-uniform flag as a scalar value, so that branches on it are scalar
+// branches instead of per-lane exec masking.
+__device__ __forceinline__ bool uniform(bool v) { return __builtin_amdgcn_readfirstlane((int)v) != 0; }
+
 // Bias, masks, online softmax and P.V for one 32-key subtile starting at key
 // js. `s` holds S^T (lane: keys js + 16 (r/8) + 8 (lane>>5) + r%8 of column
-// lane & 31); `rb` is the lane's staged bias row (rel_row_ptr) or null when no
-// distance of the subtile is below R. `vread(dt, c)` returns the P.V A
-// operand: V^T rows 32 dt + (lane & 31), keys 16 c + 8 (lane>>5) .. +8.
+// lane & 31); if `has_bias`, `rb` is the lane's staged bias row (rel_row_ptr).
+// `vread(dt, c)` returns the P.V A operand: V^T rows 32 dt + (lane & 31),
+// keys 16 c + 8 (lane>>5) .. +8.
 template <int DV, class VRead>
-__device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, const float* rb, int js, int W,
-                                           float c1, int lane, VRead vread) {
+__device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
+                                           int js, int W, float c1, int lane, VRead vread) {
     const int hh = lane >> 5;
-    const bool need_mask = C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W);
+    const bool need_mask = uniform(C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W));
 
     float x[16];
-    float M = -INFINITY;
+    if (uniform(has_bias)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float bterm = rb ? fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], LOG2E, -C.m_ref) : -C.m_ref;
-        float t = fmaf(s[r], c1, bterm);
-        if (need_mask) {
-            const int key = js + 16 * (r >> 3) + 8 * hh + (r & 7);
-            const bool vis = key <= C.pos && (W == 0 || C.pos - key < W);
-            t = vis ? t : -INFINITY;
-        }
-        x[r] = t;
-        M = fmaxf(M, t);
+        for (int r = 0; r < 16; ++r)
+            x[r] = fmaf(s[r], c1, fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], LOG2E, -C.m_ref));
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], c1, -C.m_ref);
     }
+    if (need_mask) {
+        const int d0 = C.pos - (js + 8 * hh);  // distance of register 0's key
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = d0 - (16 * (r >> 3) + (r & 7));
+            const bool vis = d >= 0 && (W == 0 || d < W) && C.pos >= 0;
+            x[r] = vis ? x[r] : -INFINITY;
+        }
+    }
+    float M = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
     M = fmaxf(M, xor32(M));
 
     const bool trig = (M > TAU) || (!C.m_set && M > -INFINITY);
@@ -357,7 +370,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     const int h = g * A.G + hl;
     const int qa = q0 + (wid / A.hpw) * 32;
     const int qb = min(qa + 32, q_len) - 1;
-    const bool wave_active = qa < q_len;
+    const bool wave_active = uniform(qa < q_len);
     const int r = qa + n;
     const bool real = r < q_len;
     const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
@@ -426,8 +439,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
             if (ok_cur && !masked_all(C, js, A.W)) {
                 const f32x16 s = qk_lds(Ks + 32 * sub * KROW, C.qreg, lane);
                 __builtin_amdgcn_wave_barrier();
-                const float* rb = cur_rel ? rel_row_ptr(Rw, C.pos, lane) : nullptr;
-                softmax_pv<DV>(C, s, rb, js, A.W, A.c1, lane, [&](int dt, int c) {
+                softmax_pv<DV>(C, s, cur_rel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane, [&](int dt, int c) {
                     return v_operand(Vs, vrow<DV>(), 32 * sub + 16 * c, 32 * dt, lane);
                 });
             }
@@ -559,13 +571,9 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
         RelRegs rr;
         if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
         const f32x16 s = qk_regs(kr, C.qreg);
-        const float* rb = nullptr;
-        if (brel) {
-            rel_store(Rw, rr, lane);
-            rb = rel_row_ptr(Rw, C.pos, lane);
-        }
+        if (brel) rel_store(Rw, rr, lane);
         __builtin_amdgcn_wave_barrier();
-        softmax_pv<DV>(C, s, rb, js, A.W, A.c1, lane,
+        softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
                        [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
         __builtin_amdgcn_wave_barrier();
     }
