@@ -40,6 +40,29 @@ DECODE = "paged_decode_16x8k_128k_disjoint"
 DQK = 128
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_paged_decode_16_disjoint_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode split kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source
+    has changed since those counters were taken."""
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
 def visible_counts(q_lens, seq_lens, W, R):
     """Per call: visible (row, key) pairs, visible keys with a bias entry
     (distance < R), and the distinct keys any query sees (for K/V bytes)."""
@@ -283,7 +306,7 @@ def main():
         achieved = b_split / t_split / 1e9
         roofline = {"kernel": "decode_split_kernel<128>", "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                    "traffic": None, "algorithmic_bytes_per_launch": b_split,
+                    "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b_split,
                     "avg_launch_ms": round(ms["decode_split"], 4)}
     else:
         achieved = b_pre / t_pre / 1e9

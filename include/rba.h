@@ -183,7 +183,7 @@ int rba_validate_decode(const rba_attn_params* params,
  * Split plan (host only, pure function). Returns the number of KV splits
  * rba_decode uses for num_splits = 0 on a device with `num_cus` compute units:
  * enough (sequence, KV head, split) work units to give every CU several, no
- * more splits than KV blocks, at most 256. Returns a negative RBA_ERR_* code on
+ * fewer than ~16 KV blocks per split, at most 256. Returns a negative RBA_ERR_* code on
  * bad arguments.
  */
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,

@@ -547,16 +547,25 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
     const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
-    int tab_base = s_lo;
-    int tabv = (s_lo + lane < s_hi) ? tab[s_lo + lane] : -1;
-    for (int kb = s_lo; kb < s_hi; ++kb) {
+    // This wave's subtiles that are not entirely masked form one run of blocks.
+    int ka = s_lo, kz = s_hi - 1;
+    while (ka <= kz && masked_all(C, ka * BS + 32 * wid, A.W)) ++ka;
+    while (kz >= ka && masked_all(C, kz * BS + 32 * wid, A.W)) --kz;
+
+    // split's block-table slice, lane i = entry tab_base + i
+    int tab_base = ka;
+    int tabv = (ka + lane <= kz) ? tab[ka + lane] : -1;
+    auto phys_of = [&](int kb) {
         if (kb - tab_base >= 64) {
             tab_base += 64;
-            tabv = (tab_base + lane < s_hi) ? tab[tab_base + lane] : -1;
+            tabv = (tab_base + lane <= kz) ? tab[tab_base + lane] : -1;
         }
+        return __builtin_amdgcn_readlane(tabv, kb - tab_base);
+    };
+
+    for (int kb = ka; kb <= kz; ++kb) {
         const int js = kb * BS + 32 * wid;
-        if (masked_all(C, js, A.W)) continue;
-        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        const int phys = phys_of(kb);
         if (phys < 0 || phys >= A.num_blocks) {
             bad = true;
             continue;
@@ -630,7 +639,10 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the splits: one wave per (row, head).
+// Log-sum-exp merge of the splits: one wave per (row, head). Lane s holds the
+// weight exp(lse_s - LSE) of split s (64 splits per pass); the weights are then
+// broadcast with readlane while every lane accumulates its value dimensions,
+// so the partial-output loads of consecutive splits are independent.
 // ---------------------------------------------------------------------------
 template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
@@ -641,11 +653,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
     const float* os = A.part_o + pair * A.splits * DV;
 
     float M = -INFINITY;
-    for (int s = lane; s < A.splits; s += 64) M = fmaxf(M, ls[s]);
+    bool nan_seen = false;
+    for (int s = lane; s < A.splits; s += 64) {
+        const float v = ls[s];
+        M = fmaxf(M, v);
+        nan_seen = nan_seen || (v != v);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    bool nan_seen = false;
-    for (int s = lane; s < A.splits; s += 64) nan_seen = nan_seen || (ls[s] != ls[s]);
     nan_seen = __any(nan_seen);
 
     constexpr int PER = DV / 64;
@@ -653,14 +668,21 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
     float den = 0.f;
-    if (M > -INFINITY) {
-        for (int s = 0; s < A.splits; ++s) {
-            const float w = __builtin_amdgcn_exp2f((ls[s] - M) * LOG2E);
-            den += w;
+    for (int base = 0; base < A.splits; base += 64) {
+        const int s = base + lane;
+        const float w = (s < A.splits && M > -INFINITY) ? __builtin_amdgcn_exp2f((ls[s] - M) * LOG2E) : 0.f;
+        den += w;
+        const int cnt = min(64, A.splits - base);
+        const float* ob = os + (long long)base * DV + lane;
+#pragma unroll 8
+        for (int k = 0; k < cnt; ++k) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc[k] += w * os[s * DV + lane + 64 * k];
+            for (int p = 0; p < PER; ++p) acc[p] += wk * ob[k * DV + 64 * p];
         }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
     const float inv = nan_seen ? NAN : 1.f / den;
 #pragma unroll
     for (int k = 0; k < PER; ++k) A.out[pair * DV + lane + 64 * k] = acc[k] * inv;
