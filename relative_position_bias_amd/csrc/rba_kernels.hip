@@ -65,15 +65,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int BS = 128;        // keys per cache block
 constexpr int DQK = 128;       // query/key head size
 constexpr int KROW = DQK + 8;  // bf16 per LDS row of K (16-byte pad)
-constexpr int RROW = 40;       // floats per LDS row of a staged rel band (36 used)
+constexpr int RROW = 36;       // floats per LDS row of a staged rel band (36 mod 64 banks spreads 16 rows)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
-constexpr float TAU = 8.0f;    // lazy-rescale threshold, log2 units
+constexpr float TAU = 16.0f;   // lazy-rescale threshold, log2 units (p <= 2^16)
 
-// bf16 per LDS row of V in its natural layout; the 32-byte pad puts the 4
-// rows one transposed read touches on distinct banks.
+// bf16 per LDS row of V in its natural layout. A transposed read has each
+// half-wave touch 4 consecutive rows x 64 bytes; a row stride of DV + 32 bf16
+// (16 mod 64 dwords for DV = 64 and 128) puts those 4 spans on disjoint banks.
 template <int DV>
-constexpr int vrow() { return DV + 16; }
+constexpr int vrow() { return DV + 32; }
 
 __device__ __forceinline__ int perm32(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -124,7 +125,9 @@ struct Cols {
     bool m_set;
 };
 
-__device__ __forceinline__ bool uniform(bool v);
+// Wave-uniform flag as a scalar value, so that branches on it are scalar
+// branches instead of per-lane exec masking.
+__device__ __forceinline__ bool uniform(bool v) { return __builtin_amdgcn_readfirstlane((int)v) != 0; }
 
 template <int DV>
 __device__ __forceinline__ bool masked_all(const Cols<DV>& C, int js, int W) {
@@ -192,23 +195,21 @@ __device__ __forceinline__ f32x16 qk_regs(const bf16x8 (&kreg)[8], const bf16x8 
     return s;
 }
 
-// Wave-uniform flag as a scalar value, so that branches on it are scalar
-// branches instead of per-lane exec masking.
-__device__ __forceinline__ bool uniform(bool v) { return __builtin_amdgcn_readfirstlane((int)v) != 0; }
-
-// Bias, masks, online softmax and P.V for one 32-key subtile starting at key
-// js. `s` holds S^T (lane: keys js + 16 (r/8) + 8 (lane>>5) + r%8 of column
-// lane & 31); if `has_bias`, `rb` is the lane's staged bias row (rel_row_ptr).
-// `vread(dt, c)` returns the P.V A operand: V^T rows 32 dt + (lane & 31),
-// keys 16 c + 8 (lane>>5) .. +8.
-template <int DV, class VRead>
-__device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
-                                           int js, int W, float c1, int lane, VRead vread) {
+// Softmax of one 32-key subtile starting at key js, in three steps so that
+// several column tiles can be interleaved:
+//   sm_scores  x = log2-domain logits relative to the reference max (bias and
+//              masks applied); returns the column's subtile max (both halves).
+//   sm_rescale moves the reference max of columns whose subtile max exceeds
+//              it by more than TAU (or that see their first key), rescaling
+//              the accumulator; callers skip it when no lane needs it.
+//   sm_probs   p = exp2(x), row sums, and the bf16 B operands of P.V.
+// `s` holds S^T (lane: keys js + 16 (r/8) + 8 (lane>>5) + r%8 of column
+// lane & 31); if `has_bias`, `rb` is the lane's staged bias row.
+template <int DV>
+__device__ __forceinline__ float sm_scores(const Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
+                                           bool need_mask, int js, int W, float c1, int lane, float (&x)[16]) {
     const int hh = lane >> 5;
-    const bool need_mask = uniform(C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W));
-
-    float x[16];
-    if (uniform(has_bias)) {
+    if (has_bias) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             x[r] = fmaf(s[r], c1, fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], LOG2E, -C.m_ref));
@@ -228,32 +229,74 @@ __device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool ha
     float M = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
-    M = fmaxf(M, xor32(M));
+    return fmaxf(M, xor32(M));
+}
 
-    const bool trig = (M > TAU) || (!C.m_set && M > -INFINITY);
-    if (__any(trig)) {
-        const float delta = trig ? M : 0.f;
-        const float alpha = trig ? (C.m_set ? __builtin_amdgcn_exp2f(-delta) : 0.f) : 1.f;
+template <int DV>
+__device__ __forceinline__ bool sm_trigger(const Cols<DV>& C, float M) {
+    return (M > TAU) || (!C.m_set && M > -INFINITY);
+}
+
+// First visible keys of a column: take their max as the reference. The
+// accumulator and row sum are still zero, so nothing needs rescaling.
+template <int DV>
+__device__ __forceinline__ void sm_init_ref(Cols<DV>& C, float& M, float (&x)[16]) {
+    if (!C.m_set && M > -INFINITY) {
 #pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt) C.O[dt] *= alpha;
-        C.l_sum *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] -= delta;
-        C.m_ref += delta;
-        C.m_set = C.m_set || trig;
+        for (int r = 0; r < 16; ++r) x[r] -= M;
+        C.m_ref += M;
+        C.m_set = true;
+        M = 0.f;
     }
+}
 
+template <int DV>
+__device__ __forceinline__ void sm_rescale(Cols<DV>& C, float M, float (&x)[16]) {
+    const bool trig = sm_trigger(C, M);
+    const float delta = trig ? M : 0.f;
+    const float alpha = trig ? (C.m_set ? __builtin_amdgcn_exp2f(-delta) : 0.f) : 1.f;
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt) C.O[dt] *= alpha;
+    C.l_sum *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] -= delta;
+    C.m_ref += delta;
+    C.m_set = C.m_set || trig;
+}
+
+template <int DV>
+__device__ __forceinline__ void sm_probs(Cols<DV>& C, const float (&x)[16], bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        bf16x8 pb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float p = __builtin_amdgcn_exp2f(x[8 * c + i]);
             C.l_sum += p;
-            pb[i] = (__bf16)p;
+            pb[c][i] = (__bf16)p;
         }
+    }
+}
+
+template <int DV>
+__device__ __forceinline__ bool need_mask_of(const Cols<DV>& C, int js, int W) {
+    return uniform(C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W));
+}
+
+// Single-tile softmax and P.V for one subtile; `vread(dt, c)` returns the P.V
+// A operand: V^T rows 32 dt + (lane & 31), keys 16 c + 8 (lane>>5) .. +8.
+template <int DV, class VRead>
+__device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
+                                           int js, int W, float c1, int lane, VRead vread) {
+    float x[16];
+    float M = sm_scores(C, s, uniform(has_bias), rb, need_mask_of(C, js, W), js, W, c1, lane, x);
+    if (__any(!C.m_set)) sm_init_ref(C, M, x);
+    if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+    bf16x8 pb[2];
+    sm_probs(C, x, pb);
 #pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt) C.O[dt] = mfma32(vread(dt, c), pb, C.O[dt]);
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt) C.O[dt] = mfma32(vread(dt, c), pb[c], C.O[dt]);
     }
 }
 
