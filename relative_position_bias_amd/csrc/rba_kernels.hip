@@ -30,8 +30,9 @@
 //     shear. Subtiles whose distances are all >= R skip rel entirely; subtiles
 //     that are entirely masked (causal / window) are skipped.
 //   * Online softmax in fp32 in the log2 domain with a lazy reference: the
-//     reference max moves only when a subtile's max exceeds it by > 8 (exact
-//     rearrangement; p <= 2^8), so the rescale of the accumulator is rare.
+//     reference max moves only when a subtile's max exceeds it by > 16 (exact
+//     rearrangement; p <= 2^16), so the rescale of the accumulator is rare.
+//     The column max across the two lane halves is one v_permlane32_swap.
 //   * Prefill: a workgroup of 8 waves shares each 128-key K/V block in LDS for
 //     up to 8 query heads of one KV head (GQA packing) and 32..256 query rows.
 //     The next block's K/V and the next subtile's rel are prefetched into
@@ -93,6 +94,23 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Workgroup barrier that waits only for this wave's LDS traffic: global
+// prefetch loads stay in flight across it (the fence of __syncthreads would
+// drain them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// max(v, v of lane ^ 32): one v_permlane32_swap of two copies of v hands every
+// lane both halves (first result: the low half's value, second: the high
+// half's), a short VALU hop instead of an LDS-routed lane shuffle. The
+// elements are copied to scalars before the bit casts (a bit cast of a vector
+// element reads the vector's first element).
+__device__ __forceinline__ float halves_max(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
 // P.V A operand from V in natural layout [key][dim] (row stride `vs` bf16):
 // lane gets V[key0 + 8 (lane>>5) + 0..7][dv0 + (lane & 31)] as 8 bf16, via two
 // transposed LDS reads. ds_read_b64_tr_b16 hands lane i of each 16-lane group
@@ -125,18 +143,19 @@ struct Cols {
     bool m_set;
 };
 
-// Wave-uniform flag as a scalar value, so that branches on it are scalar
-// branches instead of per-lane exec masking.
-__device__ __forceinline__ bool uniform(bool v) { return __builtin_amdgcn_readfirstlane((int)v) != 0; }
+// The tile tests below read only wave-uniform values (the wave index is
+// taken with readfirstlane, so w_lo / w_hi / phantom live in scalar
+// registers): they compile to scalar compares and branches, with no round
+// trip through a vector register.
 
 template <int DV>
 __device__ __forceinline__ bool masked_all(const Cols<DV>& C, int js, int W) {
-    return uniform(js > C.w_hi || (W > 0 && C.w_lo - (js + 31) >= W));
+    return js > C.w_hi || (W > 0 && C.w_lo - (js + 31) >= W);
 }
 
 template <int DV>
 __device__ __forceinline__ bool bias_on(const Cols<DV>& C, int js, int R) {
-    return uniform(C.w_lo - (js + 31) < R);
+    return C.w_lo - (js + 31) < R;
 }
 
 // rel pieces one 32-key subtile needs for this lane's own row: row n needs
@@ -229,7 +248,7 @@ __device__ __forceinline__ float sm_scores(const Cols<DV>& C, const f32x16& s, b
     float M = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
-    return fmaxf(M, xor32(M));
+    return halves_max(M);
 }
 
 template <int DV>
@@ -279,7 +298,7 @@ __device__ __forceinline__ void sm_probs(Cols<DV>& C, const float (&x)[16], bf16
 
 template <int DV>
 __device__ __forceinline__ bool need_mask_of(const Cols<DV>& C, int js, int W) {
-    return uniform(C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W));
+    return C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W);
 }
 
 // Single-tile softmax and P.V for one subtile; `vread(dt, c)` returns the P.V
@@ -288,9 +307,11 @@ template <int DV, class VRead>
 __device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
                                            int js, int W, float c1, int lane, VRead vread) {
     float x[16];
-    float M = sm_scores(C, s, uniform(has_bias), rb, need_mask_of(C, js, W), js, W, c1, lane, x);
-    if (__any(!C.m_set)) sm_init_ref(C, M, x);
-    if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+    float M = sm_scores(C, s, has_bias, rb, need_mask_of(C, js, W), js, W, c1, lane, x);
+    if (__any(!C.m_set || sm_trigger(C, M))) {
+        if (__any(!C.m_set)) sm_init_ref(C, M, x);
+        if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+    }
     bf16x8 pb[2];
     sm_probs(C, x, pb);
 #pragma unroll
@@ -392,7 +413,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     __shared__ __attribute__((aligned(16))) __bf16 Vs[BS * vrow<DV>()];
     __shared__ __attribute__((aligned(16))) float Rs[8 * 32 * RROW];
 
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31;
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
     int id = blockIdx.x;
     const int g = id % A.Hkv;
     id /= A.Hkv;
@@ -413,7 +434,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     const int h = g * A.G + hl;
     const int qa = q0 + (wid / A.hpw) * 32;
     const int qb = min(qa + 32, q_len) - 1;
-    const bool wave_active = uniform(qa < q_len);
+    const bool wave_active = qa < q_len;
     const int r = qa + n;
     const bool real = r < q_len;
     const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
@@ -457,9 +478,9 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     for (int kb = kb_lo; kb <= kb_hi; ++kb) {
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
-        __syncthreads();
+        lds_barrier();
         if (ok_cur) kv_store<DV>(Ks, Vs, kv, tid);
-        __syncthreads();
+        lds_barrier();
         if (kb < kb_hi) {  // prefetch the next block while this one is computed
             if (kb + 1 - tab_base >= 64) {
                 tab_base += 64;
@@ -553,7 +574,7 @@ template <int DV>
 __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
     __shared__ __attribute__((aligned(16))) char smem[DecodeLds<DV>::TOTAL];
 
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
     int id = blockIdx.x;
     const int g = id % A.Hkv;
     id /= A.Hkv;
