@@ -42,12 +42,14 @@ DQK = 128
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_paged_decode_16_disjoint_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_kernels.hip")
+HOST_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_host.cpp")
 
 
 def measured_traffic():
     """HBM bytes per launch of the decode split kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source
-    has changed since those counters were taken."""
+    or the host code (which sets the launch, e.g. the split count) has changed
+    since those counters were taken."""
     import hashlib
 
     if not os.path.exists(TRAFFIC_FILE):
@@ -58,7 +60,8 @@ def measured_traffic():
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src:
+    host = hashlib.sha256(open(HOST_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src or kv.get("host_source_sha256") != host:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -163,7 +166,7 @@ def _sampled_prefill_work(b, rows):
     return flops, nbytes
 
 
-def workload_report(name, steps, warmup, dev):
+def workload_report(name, steps, warmup, dev, flush=True):
     """Per-call times of one named workload (each call timed with events on
     its stream), with algorithmic TFLOP/s, GB/s and roofline fractions."""
     import torch
@@ -178,6 +181,11 @@ def workload_report(name, steps, warmup, dev):
     else:
         calls = [(full, gpu)]
     stream = torch.cuda.current_stream()
+    # Between timed calls a 1 GiB scratch read (outside the timed region)
+    # evicts the L2 and the 256 MB Infinity Cache, so no call is served from a
+    # previous call's cached inputs. A read leaves clean lines behind; a write
+    # would leave dirty ones whose write-back lands inside the next timed call.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev) if flush else None
     res = []
     for b_cpu, b in calls:
         fn = (lambda b=b: run_prefill(b)) if b.kind == "prefill" else (lambda b=b: run_decode(b))
@@ -185,7 +193,9 @@ def workload_report(name, steps, warmup, dev):
             fn()
         torch.cuda.synchronize()
         ev = []
-        for _ in range(steps):
+        for k in range(steps):
+            if scratch is not None:
+                scratch.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -201,7 +211,7 @@ def workload_report(name, steps, warmup, dev):
                     "roof_ms": round(roof_time(f, nbytes) * 1e3, 4), "flops": f, "bytes": nbytes})
     tot = sum(r["ms_median"] for r in res)
     roof = sum(r["roof_ms"] for r in res)
-    print(json.dumps({"workload": name, "calls": res, "total_ms": round(tot, 4),
+    print(json.dumps({"workload": name, "cache_flush": flush, "calls": res, "total_ms": round(tot, 4),
                       "roofline_frac": round(roof / tot, 4),
                       "tflops_total": round(sum(r["flops"] for r in res) / tot / 1e9, 2)}), flush=True)
 
@@ -217,6 +227,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default=None,
                     help="time one named workload on its own (a report line, not the step line)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="with --workload: skip the 1 GiB cache-evicting write between timed calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -232,7 +244,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload:
-        workload_report(args.workload, args.steps, args.warmup, dev)
+        workload_report(args.workload, args.steps, args.warmup, dev, flush=not args.no_flush)
         return
     t_gen = time.perf_counter()
     pre_cpu = W.build(PREFILL)

@@ -181,10 +181,12 @@ int rba_validate_decode(const rba_attn_params* params,
 
 /*
  * Split plan (host only, pure function). Returns the number of KV splits
- * rba_decode uses for num_splits = 0 on a device with `num_cus` compute units:
- * enough (sequence, KV head, split) work units to give every CU several, no
- * fewer than ~16 KV blocks per split, at most 256. Returns a negative RBA_ERR_* code on
- * bad arguments.
+ * rba_decode uses for num_splits = 0 on a device with `num_cus` compute units.
+ * Work units are (sequence, KV head, 32-column group, split); two run per CU
+ * at a time. If one such round (2 * num_cus units) covers max_seq_len with at
+ * most 128 blocks per split it is used as is; otherwise splits of ~32 blocks
+ * of max_seq_len. Never fewer than ~16 blocks per split, at most 256 splits.
+ * Returns a negative RBA_ERR_* code on bad arguments.
  */
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,
                                int32_t max_seq_len, int32_t num_cus);

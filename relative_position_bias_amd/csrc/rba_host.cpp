@@ -109,12 +109,19 @@ int64_t decode_nb_eff(const rba_attn_params* p, int32_t n_q, int32_t max_seq_len
 
 int32_t plan_splits(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t max_seq_len,
                     int32_t num_cus) {
+    // Two decode workgroups are resident per CU. If one resident round of
+    // workgroups covers the longest sequence with at most 128 blocks per
+    // split, use exactly that round (no tail). Otherwise the lengths are long
+    // compared with the machine: cut them into 32-block splits so that long
+    // and short sequences spread over many workgroups. Always at least ~16
+    // blocks per split and at most 256 splits.
     const int64_t G = p->num_heads_q / p->num_heads_kv;
     const int64_t n_cg = ceil_div(G * n_q, 32);
     const int64_t nb_eff = decode_nb_eff(p, n_q, max_seq_len);
     const int64_t units = (int64_t)batch * p->num_heads_kv * n_cg;
-    int64_t want = ceil_div(8LL * num_cus, units);
-    int64_t cap = ceil_div(nb_eff, 16);  // keep at least ~16 blocks per split
+    const int64_t fill = (2LL * num_cus) / units;
+    int64_t want = (fill >= 1 && ceil_div(nb_eff, fill) <= 128) ? fill : ceil_div(nb_eff, 32);
+    int64_t cap = ceil_div(nb_eff, 16);
     if (cap > 256) cap = 256;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;

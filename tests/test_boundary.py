@@ -150,11 +150,13 @@ def test_workspace_size_formula():
 
 
 def test_split_plan():
-    # 16 sequences x 8 KV heads, up to 1024 blocks: 8 work units per CU
-    assert rba.plan_splits(32, 8, 128, 1024, 0, 0.1, 16, 1, 131072, 256) == 16
-    # batch 1, 100K context: bounded by ~16 blocks per split
+    # 16 sequences x 8 KV heads, up to 1024 blocks: one round of 512 units
+    # would need 256 blocks per split, so 32-block splits
+    assert rba.plan_splits(32, 8, 128, 1024, 0, 0.1, 16, 1, 131072, 256) == 32
+    # batch 1, 100K context: one round would be 64 splits, bounded by ~16 blocks per split
     assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 1, 4, 100000, 256) == 49
-    assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 8, 4, 100000, 256) == 32
+    # batch 8: exactly one round of 2 x 256 units (98 blocks per split)
+    assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 8, 4, 100000, 256) == 8
     # a window bounds the blocks any query group can see
     assert rba.plan_splits(32, 8, 128, 512, 512, 0.1, 1, 1, 131072, 256) == 1
     for batch in (1, 3, 64, 1000):
