@@ -703,6 +703,283 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
 }
 
 // ---------------------------------------------------------------------------
+// Split-KV decode, 16-column variant (G * n_q <= 16, e.g. one token of 4
+// query heads per KV head). Same work split as decode_split_kernel, but the
+// scores use v_mfma_f32_16x16x32_bf16 with 16 (head, token) columns per wave,
+// which halves the query, score and accumulator registers; the room goes to a
+// prefetch of the next block's K operands and V subtile, so every wave keeps
+// two blocks of loads in flight.
+//
+// Layouts (lane l, column c = l & 15, lane group q = l >> 4):
+//   S^T half h (16 keys x 16 columns): MFMA row m holds key 8 (m/4) + 4 h +
+//   m%4, so lane l gets keys 8 q + 4 h + j (j = 0..3): the lane's 8 keys of
+//   the 32-key subtile are 8 q .. 8 q + 7, exactly the B operand of P.V.
+//   O^T tile t (16 dims x 16 columns): lane holds dims 16 t + 4 q + j.
+// ---------------------------------------------------------------------------
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4v mfma16(const bf16x8& a, const bf16x8& b, const f32x4v& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column's 4 groups)
+__device__ __forceinline__ float groups_max(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t a = r[0], b = r[1];
+    return halves_max(fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+}
+
+__device__ __forceinline__ float groups_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t a = r[0], b = r[1];
+    const float s = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+    const uint32_t w = __builtin_bit_cast(uint32_t, s);
+    const auto r2 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    const uint32_t c = r2[0], d = r2[1];
+    return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+
+// K operands of one 32-key subtile: kr[2 h + ... ] in order (h, s):
+// lane loads key 32 sub + 8 (m/4) + 4 h + m%4 (m = l & 15), dims 32 s + 8 q.
+__device__ __forceinline__ void load_k16(bf16x8 (&kr)[8], const uint16_t* kblk, int sub, int lane) {
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint16_t* row = kblk + (32 * sub + 8 * (m >> 2) + 4 * h + (m & 3)) * DQK + 8 * q;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kr[4 * h + st] = *reinterpret_cast<const bf16x8*>(row + 32 * st);
+    }
+}
+
+// P.V A operand for dim tile t from V in natural layout (row stride vs):
+// lane gets V[8 q + 0..7][16 t + (l & 15)] via two transposed reads (lane j
+// of a 16-lane group takes element j%4 from the address of lane 4k + j/4).
+__device__ __forceinline__ bf16x8 v16_operand(const __bf16* Vs, int vs, int t, int lane) {
+    const int q = lane >> 4, j = lane & 15;
+    const __bf16* p = Vs + (8 * q + (j >> 2)) * vs + 16 * t + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * vs));
+    union {
+        s16x4 h[2];
+        bf16x8 v;
+    } u;
+    u.h[0] = lo;
+    u.h[1] = hi;
+    return u.v;
+}
+
+template <int DV>
+struct Decode16Lds {
+    static constexpr int V_BYTES = 32 * vrow<DV>() * 2;
+    static constexpr int MERGE = 4 * 16 * DV * 4 + 2 * 4 * 16 * 4;
+    static constexpr int TOTAL = (4 * V_BYTES > MERGE) ? 4 * V_BYTES : MERGE;
+};
+
+template <int DV>
+__global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs A) {
+    __shared__ __attribute__((aligned(16))) char smem[Decode16Lds<DV>::TOTAL];
+
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, q = lane >> 4;
+    int id = blockIdx.x;
+    const int g = id % A.Hkv;
+    id /= A.Hkv;
+    const int b = id % A.batch;
+    id /= A.batch;
+    const int split = id / A.n_cg;  // n_cg == 1 for this variant
+
+    const int L = A.seq_lens[b];
+    const int ncols = A.G * A.n_q;
+    const bool real = c < ncols;
+    const int tt = real ? c / A.G : 0;
+    const int h = g * A.G + (real ? c % A.G : 0);
+    const long long trow = (long long)(b * A.n_q + tt) * A.Hq + h;
+    const int pos = real ? L - A.n_q + tt : -1;
+    const float* relrow = A.rel + trow * A.R;
+    // wave-uniform column range (positions of the first and last real column)
+    const int w_lo = L - A.n_q, w_hi = L - A.n_q + (ncols - 1) / A.G;
+    const bool phantom = ncols < 16;
+
+    bf16x8 qreg[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (real) {
+            qreg[st] = *reinterpret_cast<const bf16x8*>(A.q + trow * DQK + 32 * st + 8 * q);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qreg[st][i] = (__bf16)0.f;
+        }
+    }
+    f32x4v O[DV / 16];
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t) O[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    float m_ref = 0.f, l_sum = 0.f;
+    bool m_set = false;
+
+    const int nb = (L + BS - 1) / BS;
+    const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
+    const int s_lo = kb_first + split * A.bps;
+    const int s_hi = min(s_lo + A.bps, nb);
+    __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Decode16Lds<DV>::V_BYTES);
+    const int* tab = A.tables + (long long)b * A.max_blocks;
+    bool bad = false;
+
+    auto masked_all16 = [&](int js) { return js > w_hi || (A.W > 0 && w_lo - (js + 31) >= A.W); };
+    int ka = s_lo, kz = s_hi - 1;
+    while (ka <= kz && masked_all16(ka * BS + 32 * wid)) ++ka;
+    while (kz >= ka && masked_all16(kz * BS + 32 * wid)) --kz;
+
+    int tab_base = ka;
+    int tabv = (ka + lane <= kz) ? tab[ka + lane] : -1;
+    auto block_base = [&](int kb, bool& okk) -> size_t {
+        if (kb - tab_base >= 64) {
+            tab_base += 64;
+            tabv = (tab_base + lane <= kz) ? tab[tab_base + lane] : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        okk = phys >= 0 && phys < A.num_blocks;
+        return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
+    };
+
+    bf16x8 kr[8];
+    VSub<DV> vs;
+    bool ok_cur = false;
+    if (ka <= kz) {
+        const size_t base = block_base(ka, ok_cur);
+        if (ok_cur) {
+            load_k16(kr, A.k + base * DQK, wid, lane);
+            load_v_sub<DV>(vs, A.v + base * DV, wid, L - ka * BS, lane);
+        }
+    }
+#pragma unroll 1
+    for (int kb = ka; kb <= kz; ++kb) {
+        const int js = kb * BS + 32 * wid;
+        bool ok_next = false;
+        const size_t base_next = kb < kz ? block_base(kb + 1, ok_next) : 0;
+        if (!ok_cur) {
+            bad = true;
+            if (ok_next) {
+                load_k16(kr, A.k + base_next * DQK, wid, lane);
+                load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+            }
+            ok_cur = ok_next;
+            continue;
+        }
+        store_v_sub<DV>(Vw, vs, lane);
+        if (ok_next) load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+        // S^T halves
+        f32x4v S[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            S[hh] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) S[hh] = mfma16(kr[4 * hh + st], qreg[st], S[hh]);
+        }
+        if (ok_next) load_k16(kr, A.k + base_next * DQK, wid, lane);
+        // logits (log2 units, relative to the reference), bias, masks
+        const bool brel = w_lo - (js + 31) < A.R;
+        const bool nmask = phantom || (js + 31 > w_lo) || (A.W > 0 && w_hi - js >= A.W);
+        const int d0 = pos - (js + 8 * q);  // distance of the lane's key i is d0 - i
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = S[i >> 2][i & 3] * A.c1 - m_ref;
+        if (brel) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int d = d0 - i;
+                const float rv = relrow[min(max(d, 0), A.R - 1)];
+                x[i] += (d >= 0 && d < A.R && pos >= 0) ? rv * LOG2E : 0.f;
+            }
+        }
+        if (nmask) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int d = d0 - i;
+                const bool vis = d >= 0 && (A.W == 0 || d < A.W) && pos >= 0;
+                x[i] = vis ? x[i] : -INFINITY;
+            }
+        }
+        float M = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) M = fmaxf(M, x[i]);
+        M = groups_max(M);
+        const bool trig = (M > TAU) || (!m_set && M > -INFINITY);
+        if (__any(trig)) {
+            // first keys of a column set its reference; a later jump moves it
+            const float delta = trig ? M : 0.f;
+            const float alpha = trig ? (m_set ? __builtin_amdgcn_exp2f(-delta) : 0.f) : 1.f;
+#pragma unroll
+            for (int t = 0; t < DV / 16; ++t) O[t] *= alpha;
+            l_sum *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] -= delta;
+            m_ref += delta;
+            m_set = m_set || trig;
+        }
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(x[i]);
+            l_sum += pv;
+            pb[i] = (__bf16)pv;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < DV / 16; ++t) O[t] = mfma16(v16_operand(Vw, vrow<DV>(), t, lane), pb, O[t]);
+        __builtin_amdgcn_wave_barrier();
+        ok_cur = ok_next;
+    }
+
+    // Merge the four waves' partial states through LDS.
+    __syncthreads();
+    float* Om = reinterpret_cast<float*>(smem);   // [4][16][DV]
+    float* Mm = Om + 4 * 16 * DV;                 // [4][16] reference max (or -inf)
+    float* Lm = Mm + 4 * 16;                      // [4][16] row sums
+    const float l_tot = groups_sum(l_sum);
+    const bool any_bad = __syncthreads_or(bad);
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = O[t][j];
+        *reinterpret_cast<f32x4*>(Om + (wid * 16 + c) * DV + 16 * t + 4 * q) = o;
+    }
+    if (q == 0) {
+        Mm[wid * 16 + c] = m_set ? m_ref : -INFINITY;
+        Lm[wid * 16 + c] = l_tot;
+    }
+    __syncthreads();
+
+    for (int e = tid; e < 16 * DV; e += 256) {
+        const int col = e / DV, dv = e % DV;
+        if (col >= ncols) continue;
+        float mw[4], Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = Mm[w * 16 + col];
+            Mx = fmaxf(Mx, mw[w]);
+        }
+        float den = 0.f, num = 0.f;
+        if (Mx > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = __builtin_amdgcn_exp2f(mw[w] - Mx);  // exp2(-inf) = 0
+                den += f * Lm[w * 16 + col];
+                num += f * Om[(w * 16 + col) * DV + dv];
+            }
+        }
+        const int ctt = col / A.G, chl = col % A.G;
+        const long long prow = ((long long)(b * A.n_q + ctt) * A.Hq + (g * A.G + chl)) * A.splits + split;
+        A.part_o[prow * DV + dv] = any_bad ? NAN : (Mx > -INFINITY ? num / den : 0.f);
+        if (dv == 0) {
+            A.part_lse[prow] = any_bad ? NAN : (Mx > -INFINITY ? (Mx + __log2f(den)) * LN2 : -INFINITY);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp merge of the splits: one wave per (row, head). Lane s holds the
 // weight exp(lse_s - LSE) of split s (64 splits per pass); the weights are then
 // broadcast with readlane while every lane accumulates its value dimensions,
@@ -769,6 +1046,14 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.Hkv * a.n_cg * a.splits;
     if (grid <= 0) return hipSuccess;
+    if (a.G * a.n_q <= 16) {  // one 16-column group (n_cg == 1)
+        if (dv == 128) {
+            hipLaunchKernelGGL(decode16_split_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(decode16_split_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     if (dv == 128) {
         hipLaunchKernelGGL(decode_split_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
     } else {

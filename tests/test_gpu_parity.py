@@ -97,6 +97,8 @@ DECODE_GRID = [
     (4, 3, [3, 250, 520, 1300], 16, 4, 128, 256, 300, None),
     (2, 8, [900, 2000], 48, 8, 128, 512, 0, None),      # G = 6, 48 columns: 2 column groups
     (5, 2, [128, 256, 384, 4000, 77], 8, 8, 64, 64, 128, 64),   # G = 1, aliased pool
+    (2, 4, [300, 1100], 16, 4, 128, 256, 0, None),      # G * n_q = 16: the 16-column kernel's limit
+    (2, 5, [300, 1100], 16, 4, 64, 256, 0, None),       # G * n_q = 20: the 32-column kernel, one group
 ]
 
 
