@@ -40,7 +40,7 @@ DECODE = "paged_decode_16x8k_128k_disjoint"
 DQK = 128
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_paged_decode_16_disjoint_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode16_split_kernel_paged_decode_16_disjoint_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_kernels.hip")
 HOST_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_host.cpp")
 
@@ -316,7 +316,9 @@ def main():
     # dominant kernel: the one with the larger share of the step
     if t_split >= t_pre:
         achieved = b_split / t_split / 1e9
-        roofline = {"kernel": "decode_split_kernel<128>", "bound": "hbm", "achieved": round(achieved, 1),
+        # G * n_q <= 16 runs the 16-column split kernel
+        kname = "decode16_split_kernel<128>" if dec.Hq // dec.Hkv * dec.n_q <= 16 else "decode_split_kernel<128>"
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b_split,
                     "avg_launch_ms": round(ms["decode_split"], 4)}
