@@ -109,9 +109,14 @@ int64_t decode_nb_eff(const rba_attn_params* p, int32_t n_q, int32_t max_seq_len
 
 int32_t plan_splits(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t max_seq_len,
                     int32_t num_cus) {
-    // Two decode workgroups are resident per CU. If one resident round of
-    // workgroups covers the longest sequence with at most 128 blocks per
-    // split, use exactly that round (no tail). Otherwise the lengths are long
+    // Up to two decode workgroups are resident per CU. If one workgroup per
+    // CU covers the longest sequence with at most 32 blocks per split, use
+    // exactly that (every CU gets the same work, and the per-workgroup start
+    // and merge costs are paid once per CU); this needs a variant that keeps
+    // the next block's loads in flight (G * n_q <= 16, or dv <= 64), since a
+    // lone workgroup otherwise has too few loads outstanding. Next, if one
+    // round of two workgroups per CU covers it with at most 128 blocks per
+    // split, use that round (no tail). Otherwise the lengths are long
     // compared with the machine: cut them into 32-block splits so that long
     // and short sequences spread over many workgroups. Always at least ~16
     // blocks per split and at most 256 splits.
@@ -119,8 +124,15 @@ int32_t plan_splits(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_
     const int64_t n_cg = ceil_div(G * n_q, 32);
     const int64_t nb_eff = decode_nb_eff(p, n_q, max_seq_len);
     const int64_t units = (int64_t)batch * p->num_heads_kv * n_cg;
-    const int64_t fill = (2LL * num_cus) / units;
-    int64_t want = (fill >= 1 && ceil_div(nb_eff, fill) <= 128) ? fill : ceil_div(nb_eff, 32);
+    const bool prefetching = G * n_q <= 16 || p->head_dim_v <= 64;
+    const int64_t fill1 = (int64_t)num_cus / units, fill2 = (2LL * num_cus) / units;
+    int64_t want;
+    if (prefetching && fill1 >= 1 && ceil_div(nb_eff, fill1) <= 32)
+        want = fill1;
+    else if (fill2 >= 1 && ceil_div(nb_eff, fill2) <= 128)
+        want = fill2;
+    else
+        want = ceil_div(nb_eff, 32);
     int64_t cap = ceil_div(nb_eff, 16);
     if (cap > 256) cap = 256;
     if (cap < 1) cap = 1;

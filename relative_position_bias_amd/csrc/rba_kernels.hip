@@ -19,25 +19,30 @@
 //     row index swapped) so that every lane ends up with 8 CONSECUTIVE keys per
 //     16-key chunk: the lane's bias values are then contiguous in its rel row,
 //     and the P.V A operand is 8 consecutive keys of one value dimension.
-//   * V stays in LDS in its natural [key][dim] layout and is read transposed
-//     with ds_read_b64_tr_b16 (gfx950): two reads give a lane the 8 keys of
-//     one value dimension that the P.V MFMA needs. No shuffles, no transposed
-//     writes.
+//   * V stays in LDS in its [key][dim] layout (the prefill rotates the
+//     64-byte groups of each row against bank conflicts) and is read
+//     transposed with ds_read_b64_tr_b16 (gfx950): two reads give a lane the
+//     8 keys of one value dimension that the P.V MFMA needs. No shuffles, no
+//     transposed writes.
 //   * The bias is "sheared": element (column n, key j) needs rel[t_n, h_n,
-//     i_n - j]. Per 32-key subtile each wave loads, with 16-byte loads, the
-//     aligned superset of its 32 rel row segments (32 rows x 36 floats), parks
-//     it in its own LDS band and reads every lane's 16 values back along the
-//     shear. Subtiles whose distances are all >= R skip rel entirely; subtiles
-//     that are entirely masked (causal / window) are skipped.
+//     i_n - j], and a lane's 8 consecutive keys are 8 consecutive (falling)
+//     distances of its own rel row. The prefill loads them straight into
+//     registers (two 16-byte loads per run); the decode loads, with 16-byte
+//     loads, the aligned superset of its 32 rel row segments (32 rows x 36
+//     floats), parks it in an LDS band and reads every lane's 16 values back
+//     along the shear. Subtiles whose distances are all >= R skip rel
+//     entirely; subtiles that are entirely masked (causal / window) are
+//     skipped.
 //   * Online softmax in fp32 in the log2 domain with a lazy reference: the
 //     reference max moves only when a subtile's max exceeds it by > 16 (exact
 //     rearrangement; p <= 2^16), so the rescale of the accumulator is rare.
 //     The column max across the two lane halves is one v_permlane32_swap.
 //   * Prefill: a workgroup of 8 waves shares each 128-key K/V block in LDS for
 //     up to 8 query heads of one KV head (GQA packing) and 32..256 query rows.
-//     The next block's K/V and the next subtile's rel are prefetched into
-//     registers while the current one is computed; the block-table slice sits
-//     in a register (one entry per lane) so no load waits on a table read.
+//     Blocks are copied HBM -> LDS by global_load_lds into double buffers
+//     (one barrier per block); the next subtile's bias comes straight into
+//     registers. The block-table slice sits in a register (one entry per
+//     lane) so no load waits on a table read.
 //   * Decode: each of the 4 waves of a workgroup streams its own 32-key
 //     subtile of every block of the split without any barrier: K goes straight
 //     from HBM into MFMA operand registers, V into a wave-private LDS tile.
@@ -65,7 +70,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BS = 128;        // keys per cache block
 constexpr int DQK = 128;       // query/key head size
-constexpr int KROW = DQK + 8;  // bf16 per LDS row of K (16-byte pad)
 constexpr int RROW = 36;       // floats per LDS row of a staged rel band (36 mod 64 banks spreads 16 rows)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
@@ -192,18 +196,6 @@ __device__ __forceinline__ void rel_store(float* Rw, const RelRegs& v, int lane)
 __device__ __forceinline__ const float* rel_row_ptr(const float* Rw, int pos, int lane) {
     const int n = lane & 31, hh = lane >> 5;
     return Rw + n * RROW + (8 + ((pos + 1) & 3) - 8 * hh);
-}
-
-// S^T for one 32-key subtile whose K rows sit in LDS (row m holds key perm32(m)).
-__device__ __forceinline__ f32x16 qk_lds(const __bf16* Ksub, const bf16x8 (&qreg)[8], int lane) {
-    f32x16 s = zero16();
-    const __bf16* krow = Ksub + (lane & 31) * KROW + 8 * (lane >> 5);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * st);
-        s = mfma32(a, qreg[st], s);
-    }
-    return s;
 }
 
 // S^T for one 32-key subtile whose K operand is already in registers.
@@ -368,50 +360,171 @@ __device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float*
 // Prefill
 // ---------------------------------------------------------------------------
 
-// One 128-key K/V block held in registers (prefetch) by a 512-thread workgroup.
+// K/V staging. Each 128-key block is copied from HBM straight into LDS with
+// global_load_lds (no register staging): every wave instruction fills 1 KB of
+// LDS, lane l landing at byte 16 l, and the lanes pick their source chunks so
+// that the LDS image has the layout the readers want.
+//   K: 128 rows x 256 bytes, no padding. Row r holds key (r & ~31) |
+//      perm32(r & 31); its logical 16-byte chunk c sits at chunk c ^ (r & 15),
+//      so the 16 rows read by one half of an MFMA operand load fall on
+//      distinct banks.
+//   V: [key][dv], 2 DV bytes per row, no padding, read transposed. The
+//      64-byte groups of a row are rotated by rot(r) = r & 3 (DV 128) or
+//      (r >> 1) & 1 (DV 64): logical group G sits at (G + rot(r)) mod
+//      (DV / 32), so the 4 consecutive rows one transposed read touches
+//      fall on distinct banks. Rows at or past the end of the sequence are
+//      copied from a 16-byte zero chunk.
+// Both are double-buffered.
+__device__ const u32x4 kZeroChunk = {0u, 0u, 0u, 0u};
+
 template <int DV>
-struct KVRegs {
-    u32x4 k[4];
-    u32x4 v[DV / 32];
+__device__ __forceinline__ int vrot(int r) {
+    return DV == 128 ? (r & 3) : ((r >> 1) & 1);
+}
+
+// P.V A operand from the rotated V: lane gets V[key0 + 8 (lane>>5) + 0..7]
+// [32 dt + (lane & 31)] (as v_operand), `vb` being the lane's offset for
+// this dt (row and group rotation folded in) and Vsub the key0 row.
+__device__ __forceinline__ bf16x8 v_operand_rot(const __bf16* Vsub, int vb, int dv) {
+    const __bf16* p = Vsub + vb;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * dv));
+    union {
+        s16x4 h[2];
+        bf16x8 v;
+    } u;
+    u.h[0] = lo;
+    u.h[1] = hi;
+    return u.v;
+}
+
+// One wave instruction of global_load_lds_dwordx4: lane l copies 16 bytes
+// from `src` to LDS byte `lds + 16 l` (lds is wave-uniform). Issued as inline
+// assembly, so the compiler neither tracks it nor adds waits for it: the
+// kernel waits for its copies itself (vm_wait_all) before the barrier that
+// publishes them.
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+// The copies are issued by the first NW waves (NW = 8 or 4), 32 / NW K and
+// 2 DV / (8 NW) V instructions each. Waves w and w + 4 share a SIMD and the
+// lower one is served first, so it reaches the block barrier early; with
+// NW = 4 the early waves issue all copies there, which balances the pair when
+// the score/softmax chain dominates (no window). With a window every subtile
+// also streams its bias from HBM and spreading the copies over all 8 waves
+// is better.
+template <int DV, int NW>
+__device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* kblk, const uint16_t* vblk,
+                                       int nvalid, int wid, int lane) {
+    if (wid >= NW) return;
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i) {
+        const int grp = wid + NW * i;  // 1 KB group: K rows 4 grp .. 4 grp + 3
+        const int r = 4 * grp + (lane >> 4);
+        const int key = (r & ~31) | perm32(r & 31);
+        const int c = (lane & 15) ^ (r & 15);
+        dma16(kblk + key * DQK + 8 * c, Ks + grp * 4 * DQK);
+    }
+    constexpr int VCH = DV / 8, RPG = 64 / VCH;  // 16-byte chunks per V row, V rows per group
+#pragma unroll
+    for (int i = 0; i < DV / (4 * NW); ++i) {
+        const int grp = wid + NW * i;
+        const int r = RPG * grp + lane / VCH;
+        const int p = lane % VCH;  // physical chunk; its logical chunk undoes the group rotation
+        const int c = 4 * (((p >> 2) - vrot<DV>(r)) & (DV / 32 - 1)) + (p & 3);
+        const void* src = r < nvalid ? static_cast<const void*>(vblk + r * DV + 8 * c) : &kZeroChunk;
+        dma16(src, Vs + grp * RPG * DV);
+    }
+}
+
+// Waits until every global load this wave issued (LDS copies included) has
+// landed.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// S^T for one 32-key subtile of the chunk-swizzled K (koff: the lane's offset
+// of operand st, row (lane & 31), logical chunk 2 st + (lane >> 5)).
+__device__ __forceinline__ f32x16 qk_swz(const __bf16* Ksub, const int (&koff)[8], const bf16x8 (&qreg)[8]) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) s = mfma32(*reinterpret_cast<const bf16x8*>(Ksub + koff[st]), qreg[st], s);
+    return s;
+}
+
+// The bias of one subtile straight from HBM into registers: register r (key
+// js + 16 (r/8) + 8 (lane>>5) + r%8) gets rel at distance pos - key. `inside`
+// (wave-uniform): every distance of every lane lies in [0, R) and no lane is
+// a phantom column; then each 8-key run is two 16-byte loads at 4-byte
+// alignment. Otherwise every element is loaded on its own from a clamped
+// index; rel_bias zeroes those at distances >= R (negative ones are masked).
+struct RelVals {
+    float v[16];
 };
 
-template <int DV>
-__device__ __forceinline__ void kv_load(KVRegs<DV>& r, const uint16_t* kblk, const uint16_t* vblk, int nvalid,
-                                        int tid) {
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ void rel_fetch(RelVals& rv, const float* relrow, int pos, int js, int R, bool inside,
+                                          int lane) {
+    const int hh = lane >> 5;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int p = tid + 512 * it;
-        r.k[it] = *reinterpret_cast<const u32x4*>(kblk + (p >> 4) * DQK + 8 * (p & 15));
-    }
+    for (int c = 0; c < 2; ++c) {
+        const int a = pos - js - 8 * hh - 16 * c - 7;
+        if (inside) {
+            const f32x4u lo = *reinterpret_cast<const f32x4u*>(relrow + a);
+            const f32x4u hi = *reinterpret_cast<const f32x4u*>(relrow + a + 4);
 #pragma unroll
-    for (int it = 0; it < DV / 32; ++it) {
-        const int p = tid + 512 * it;
-        const int key = p / (DV / 8), c = p % (DV / 8);
-        r.v[it] = key < nvalid ? *reinterpret_cast<const u32x4*>(vblk + key * DV + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) {
+                rv.v[8 * c + 7 - i] = lo[i];
+                rv.v[8 * c + 3 - i] = hi[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rv.v[8 * c + 7 - i] = relrow[min(max(a + i, 0), R - 1)];
+        }
     }
 }
 
-// K rows go to LDS row (r & ~31) | perm32(r & 31); V rows keep their order.
-template <int DV>
-__device__ __forceinline__ void kv_store(__bf16* Ks, __bf16* Vs, const KVRegs<DV>& r, int tid) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int p = tid + 512 * it;
-        const int row = p >> 4;
-        *reinterpret_cast<u32x4*>(Ks + ((row & ~31) | perm32(row & 31)) * KROW + 8 * (p & 15)) = r.k[it];
-    }
-#pragma unroll
-    for (int it = 0; it < DV / 32; ++it) {
-        const int p = tid + 512 * it;
-        *reinterpret_cast<u32x4*>(Vs + (p / (DV / 8)) * vrow<DV>() + 8 * (p % (DV / 8))) = r.v[it];
-    }
+__device__ __forceinline__ float rel_bias(const RelVals& rv, int r, int pos, int js, int R, bool inside, int lane) {
+    if (inside) return rv.v[r];
+    const int d = pos - js - 8 * (lane >> 5) - 16 * (r >> 3) - (r & 7);
+    return d < R ? rv.v[r] : 0.f;
 }
 
+// sm_scores with the bias taken from registers.
 template <int DV>
+__device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s, bool has_bias, const RelVals& rv,
+                                              bool inside, bool need_mask, int js, int W, int R, float c1, int lane,
+                                              float (&x)[16]) {
+    if (has_bias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            x[r] = fmaf(s[r], c1, fmaf(rel_bias(rv, r, C.pos, js, R, inside, lane), LOG2E, -C.m_ref));
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], c1, -C.m_ref);
+    }
+    if (need_mask) {
+        const int d0 = C.pos - (js + 8 * (lane >> 5));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = d0 - (16 * (r >> 3) + (r & 7));
+            const bool vis = d >= 0 && (W == 0 || d < W) && C.pos >= 0;
+            x[r] = vis ? x[r] : -INFINITY;
+        }
+    }
+    float M = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
+    return halves_max(M);
+}
+
+template <int DV, int NW>
 __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BS * KROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[BS * vrow<DV>()];
-    __shared__ __attribute__((aligned(16))) float Rs[8 * 32 * RROW];
+    __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 K1[BS * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 V0[BS * DV];
+    __shared__ __attribute__((aligned(16))) __bf16 V1[BS * DV];
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
     int id = blockIdx.x;
@@ -452,63 +565,88 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
     const int kb_hi = i_hi / BS;
     const int js_end = kb_hi * BS + 3 * 32;  // last subtile start
-    float* Rw = Rs + wid * 32 * RROW;
     const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
     // block-table slice of the tile (lane i = entry tab_base + i)
     int tab_base = kb_lo;
     int tabv = (kb_lo + lane <= kb_hi) ? tab[kb_lo + lane] : -1;
+    auto block_base = [&](int kb, bool& okk) -> size_t {
+        if (kb - tab_base >= 64) {
+            tab_base += 64;
+            tabv = (tab_base + lane <= kb_hi) ? tab[tab_base + lane] : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        okk = phys >= 0 && phys < A.num_blocks;
+        return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
+    };
 
     auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
+    auto rel_inside = [&](int js) { return !C.phantom && C.w_lo - js - 31 >= 0 && C.w_hi - js < A.R; };
 
-    // rel for subtile js is loaded during subtile js - 32 and parked in LDS at
-    // the start of subtile js, just before the registers take the next load.
-    RelRegs rr;
-    if (rel_active(kb_lo * BS)) rel_load(rr, C.relrow, C.pos, kb_lo * BS, A.R, lane);
-
-    KVRegs<DV> kv;
-    int phys = __builtin_amdgcn_readlane(tabv, 0);
-    bool ok = phys >= 0 && phys < A.num_blocks;
-    if (ok) {
-        const size_t base = ((size_t)phys * A.Hkv + g) * BS;
-        kv_load<DV>(kv, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, tid);
+    int koff[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) koff[st] = n * DQK + 8 * ((2 * st + (lane >> 5)) ^ (n & 15));
+    // lane offsets of the transposed V reads, one per 32-dim tile: row
+    // 8 (g >> 1) + (j >> 2) of the 16-key chunk, dims 32 dt + 16 (g & 1) + 4 (j & 3)
+    int vbo[DV / 32];
+    {
+        const int gq = lane >> 4, j = lane & 15, vr = 8 * (gq >> 1) + (j >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+            vbo[dt] = vr * DV + 32 * ((dt + vrot<DV>(vr)) & (DV / 32 - 1)) + 16 * (gq & 1) + 4 * (j & 3);
     }
 
-    for (int kb = kb_lo; kb <= kb_hi; ++kb) {
+    bool ok = false;
+    {
+        const size_t base = block_base(kb_lo, ok);
+        if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, wid, lane);
+    }
+    RelVals rv[2];  // bias of the current and of the next subtile
+    if (rel_active(kb_lo * BS)) rel_fetch(rv[0], C.relrow, C.pos, kb_lo * BS, A.R, rel_inside(kb_lo * BS), lane);
+
+    // One block: wait for its copy, start the next block's copy into the
+    // other buffers (every wave left them at this barrier), compute.
+    auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn, int kb) {
+        vm_wait_all();
+        lds_barrier();
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
-        lds_barrier();
-        if (ok_cur) kv_store<DV>(Ks, Vs, kv, tid);
-        lds_barrier();
-        if (kb < kb_hi) {  // prefetch the next block while this one is computed
-            if (kb + 1 - tab_base >= 64) {
-                tab_base += 64;
-                tabv = (tab_base + lane <= kb_hi) ? tab[tab_base + lane] : -1;
-            }
-            phys = __builtin_amdgcn_readlane(tabv, kb + 1 - tab_base);
-            ok = phys >= 0 && phys < A.num_blocks;
-            if (ok) {
-                const size_t base = ((size_t)phys * A.Hkv + g) * BS;
-                kv_load<DV>(kv, A.k + base * DQK, A.v + base * DV, L - (kb + 1) * BS, tid);
-            }
+        if (kb < kb_hi) {
+            const size_t base = block_base(kb + 1, ok);
+            if (ok) kv_dma<DV, NW>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - (kb + 1) * BS, wid, lane);
         }
-        if (!wave_active) continue;
-#pragma unroll 1
+        if (!wave_active) return;
+#pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             const int js = kb * BS + 32 * sub;
-            const bool cur_rel = rel_active(js);
-            if (cur_rel) rel_store(Rw, rr, lane);
-            if (js + 32 <= js_end && rel_active(js + 32)) rel_load(rr, C.relrow, C.pos, js + 32, A.R, lane);
+            if (js + 32 <= js_end && rel_active(js + 32))
+                rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, js + 32, A.R, rel_inside(js + 32), lane);
             if (ok_cur && !masked_all(C, js, A.W)) {
-                const f32x16 s = qk_lds(Ks + 32 * sub * KROW, C.qreg, lane);
-                __builtin_amdgcn_wave_barrier();
-                softmax_pv<DV>(C, s, cur_rel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane, [&](int dt, int c) {
-                    return v_operand(Vs, vrow<DV>(), 32 * sub + 16 * c, 32 * dt, lane);
-                });
+                const f32x16 s = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
+                float x[16];
+                float M = sm_scores_rv(C, s, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W),
+                                       js, A.W, A.R, A.c1, lane, x);
+                if (__any(!C.m_set || sm_trigger(C, M))) {
+                    if (__any(!C.m_set)) sm_init_ref(C, M, x);
+                    if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+                }
+                bf16x8 pb[2];
+                sm_probs(C, x, pb);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                    for (int dt = 0; dt < DV / 32; ++dt)
+                        C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * c) * DV, vbo[dt], DV), pb[c], C.O[dt]);
+                }
             }
-            __builtin_amdgcn_wave_barrier();
         }
+    };
+    for (int kb = kb_lo;;) {
+        step(K0, V0, K1, V1, kb);
+        if (++kb > kb_hi) break;
+        step(K1, V1, K0, V0, kb);
+        if (++kb > kb_hi) break;
     }
 
     if (!wave_active || !real) return;
@@ -627,28 +765,76 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
         return __builtin_amdgcn_readlane(tabv, kb - tab_base);
     };
 
-    for (int kb = ka; kb <= kz; ++kb) {
-        const int js = kb * BS + 32 * wid;
-        const int phys = phys_of(kb);
-        if (phys < 0 || phys >= A.num_blocks) {
-            bad = true;
-            continue;
-        }
-        const size_t base = ((size_t)phys * A.Hkv + g) * BS;
-        const bool brel = bias_on(C, js, A.R);
+    if constexpr (DV <= 64) {
+        // the dv 64 accumulators leave room for the next block's K operands
+        // and V subtile: each wave keeps two blocks of loads in flight
+        auto block_base = [&](int kb, bool& okk) -> size_t {
+            const int phys = phys_of(kb);
+            okk = phys >= 0 && phys < A.num_blocks;
+            return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
+        };
         bf16x8 kr[8];
         VSub<DV> vs;
-        load_k_sub(kr, A.k + base * DQK, wid, lane);
-        load_v_sub<DV>(vs, A.v + base * DV, wid, L - kb * BS, lane);
-        store_v_sub<DV>(Vw, vs, lane);
-        RelRegs rr;
-        if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
-        const f32x16 s = qk_regs(kr, C.qreg);
-        if (brel) rel_store(Rw, rr, lane);
-        __builtin_amdgcn_wave_barrier();
-        softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
-                       [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
-        __builtin_amdgcn_wave_barrier();
+        bool ok_cur = false;
+        if (ka <= kz) {
+            const size_t base = block_base(ka, ok_cur);
+            if (ok_cur) {
+                load_k_sub(kr, A.k + base * DQK, wid, lane);
+                load_v_sub<DV>(vs, A.v + base * DV, wid, L - ka * BS, lane);
+            }
+        }
+#pragma unroll 1
+        for (int kb = ka; kb <= kz; ++kb) {
+            const int js = kb * BS + 32 * wid;
+            bool ok_next = false;
+            const size_t base_next = kb < kz ? block_base(kb + 1, ok_next) : 0;
+            if (!ok_cur) {
+                bad = true;
+                if (ok_next) {
+                    load_k_sub(kr, A.k + base_next * DQK, wid, lane);
+                    load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+                }
+                ok_cur = ok_next;
+                continue;
+            }
+            const bool brel = bias_on(C, js, A.R);
+            RelRegs rr;
+            if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
+            store_v_sub<DV>(Vw, vs, lane);
+            if (ok_next) load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+            const f32x16 s = qk_regs(kr, C.qreg);
+            if (ok_next) load_k_sub(kr, A.k + base_next * DQK, wid, lane);
+            if (brel) rel_store(Rw, rr, lane);
+            __builtin_amdgcn_wave_barrier();
+            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
+                           [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
+            __builtin_amdgcn_wave_barrier();
+            ok_cur = ok_next;
+        }
+    } else {
+        for (int kb = ka; kb <= kz; ++kb) {
+            const int js = kb * BS + 32 * wid;
+            const int phys = phys_of(kb);
+            if (phys < 0 || phys >= A.num_blocks) {
+                bad = true;
+                continue;
+            }
+            const size_t base = ((size_t)phys * A.Hkv + g) * BS;
+            const bool brel = bias_on(C, js, A.R);
+            bf16x8 kr[8];
+            VSub<DV> vs;
+            load_k_sub(kr, A.k + base * DQK, wid, lane);
+            load_v_sub<DV>(vs, A.v + base * DV, wid, L - kb * BS, lane);
+            store_v_sub<DV>(Vw, vs, lane);
+            RelRegs rr;
+            if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
+            const f32x16 s = qk_regs(kr, C.qreg);
+            if (brel) rel_store(Rw, rr, lane);
+            __builtin_amdgcn_wave_barrier();
+            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
+                           [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
+            __builtin_amdgcn_wave_barrier();
+        }
     }
 
     // Merge the four waves' partial states through LDS.
@@ -980,54 +1166,80 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the splits: one wave per (row, head). Lane s holds the
-// weight exp(lse_s - LSE) of split s (64 splits per pass); the weights are then
-// broadcast with readlane while every lane accumulates its value dimensions,
-// so the partial-output loads of consecutive splits are independent.
+// Log-sum-exp merge of the splits: one workgroup per (row, head). Every load
+// of a pair is issued before any of them is used (each thread loads up to 4
+// split lse values and its first 16 partial-output values), so the merge
+// costs about one memory latency rather than one per batch of splits.
+// Thread (grp, d) sums dimension d over the splits grp, grp + GROUPS, ...;
+// the groups are added through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int DV>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long long pair = (long long)blockIdx.x * 4 + wid;
-    if (pair >= A.pairs) return;
-    const float* ls = A.part_lse + pair * A.splits;
-    const float* os = A.part_o + pair * A.splits * DV;
+    constexpr int GROUPS = 256 / DV;
+    constexpr int CH = 16;  // partial outputs in flight per thread
+    __shared__ float wsh[1024];
+    __shared__ float red[2][4];
+    __shared__ float part[GROUPS][DV];
+    const int tid = threadIdx.x, wid = tid >> 6;
+    const int grp = tid / DV, d = tid % DV;
+    const long long pair = blockIdx.x;
+    const int S = A.splits;  // <= 1024
+    const float* ls = A.part_lse + pair * S;
+    const float* os = A.part_o + pair * S * DV + d;
 
-    float M = -INFINITY;
-    bool nan_seen = false;
-    for (int s = lane; s < A.splits; s += 64) {
-        const float v = ls[s];
-        M = fmaxf(M, v);
-        nan_seen = nan_seen || (v != v);
+    float lv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int s = tid + 256 * k;
+        lv[k] = s < S ? ls[s] : -INFINITY;
     }
+    float v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int s = grp + GROUPS * k;
+        v[k] = s < S ? os[(long long)s * DV] : 0.f;
+    }
+
+    float M = fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3]));
+    const bool nan_here = (lv[0] != lv[0]) || (lv[1] != lv[1]) || (lv[2] != lv[2]) || (lv[3] != lv[3]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    nan_seen = __any(nan_seen);
+    if ((tid & 63) == 0) red[0][wid] = M;
+    const bool nan_seen = __syncthreads_or(nan_here);
+    M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
 
-    constexpr int PER = DV / 64;
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
     float den = 0.f;
-    for (int base = 0; base < A.splits; base += 64) {
-        const int s = base + lane;
-        const float w = (s < A.splits && M > -INFINITY) ? __builtin_amdgcn_exp2f((ls[s] - M) * LOG2E) : 0.f;
-        den += w;
-        const int cnt = min(64, A.splits - base);
-        const float* ob = os + (long long)base * DV + lane;
-#pragma unroll 8
-        for (int k = 0; k < cnt; ++k) {
-            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-            for (int p = 0; p < PER; ++p) acc[p] += wk * ob[k * DV + 64 * p];
-        }
+    for (int k = 0; k < 4; ++k) {
+        const int s = tid + 256 * k;
+        const float w = (s < S && M > -INFINITY) ? __builtin_amdgcn_exp2f((lv[k] - M) * LOG2E) : 0.f;
+        if (s < S) wsh[s] = w;
+        den += w;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
-    const float inv = nan_seen ? NAN : 1.f / den;
+    if ((tid & 63) == 0) red[1][wid] = den;
+    __syncthreads();
+    den = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+
+    float acc = 0.f;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) A.out[pair * DV + lane + 64 * k] = acc[k] * inv;
-    if (A.lse != nullptr && lane == 0) A.lse[pair] = nan_seen ? NAN : M + logf(den);
+    for (int k = 0; k < CH; ++k) {
+        const int s = grp + GROUPS * k;
+        if (s < S) acc += wsh[s] * v[k];
+    }
+#pragma unroll 8
+    for (int s = grp + GROUPS * CH; s < S; s += GROUPS) acc += wsh[s] * os[(long long)s * DV];
+    part[grp][d] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float tot = part[0][d];
+#pragma unroll
+        for (int g2 = 1; g2 < GROUPS; ++g2) tot += part[g2][d];
+        const float inv = nan_seen ? NAN : 1.f / den;
+        A.out[pair * DV + d] = tot * inv;
+        if (A.lse != nullptr && d == 0) A.lse[pair] = nan_seen ? NAN : M + logf(den);
+    }
 }
 
 }  // namespace
@@ -1035,10 +1247,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
-    if (dv == 128) {
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(512), 0, s, a);
+    const dim3 g((unsigned)grid), blk(512);
+    if (a.W > 0) {  // windowed: every subtile streams bias, all waves issue the K/V copies
+        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, 8>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<64, 8>), g, blk, 0, s, a);
     } else {
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(512), 0, s, a);
+        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, 4>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<64, 4>), g, blk, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1063,7 +1278,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s) {
-    const long long grid = ((long long)a.pairs + 3) / 4;
+    const long long grid = a.pairs;
     if (grid <= 0) return hipSuccess;
     if (dv == 128) {
         hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);

@@ -153,8 +153,12 @@ def test_split_plan():
     # 16 sequences x 8 KV heads, up to 1024 blocks: one round of 512 units
     # would need 256 blocks per split, so 32-block splits
     assert rba.plan_splits(32, 8, 128, 1024, 0, 0.1, 16, 1, 131072, 256) == 32
-    # batch 1, 100K context: one round would be 64 splits, bounded by ~16 blocks per split
-    assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 1, 4, 100000, 256) == 49
+    # batch 1, 100K context, dv 64 (a prefetching kernel): one workgroup per CU,
+    # 32 splits of 25 blocks
+    assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 1, 4, 100000, 256) == 32
+    # the same with dv 128 (no prefetch in the 32-column kernel): two per CU would
+    # be 64 splits, bounded by ~16 blocks per split
+    assert rba.plan_splits(64, 8, 128, 1024, 0, 0.1, 1, 4, 100000, 256) == 49
     # batch 8: exactly one round of 2 x 256 units (98 blocks per split)
     assert rba.plan_splits(64, 8, 64, 1024, 0, 0.1, 8, 4, 100000, 256) == 8
     # a window bounds the blocks any query group can see
