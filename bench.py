@@ -324,7 +324,7 @@ def main():
                     "avg_launch_ms": round(ms["decode_split"], 4)}
     else:
         achieved = b_pre / t_pre / 1e9
-        pname = "prefill_kernel<128, 8>" if pre.W > 0 else "prefill_kernel<128, 4>"
+        pname = "prefill_kernel<128, true>" if pre.W > 0 else "prefill_kernel<128, false>"
         roofline = {"kernel": pname, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
                     "traffic": None, "algorithmic_bytes_per_launch": b_pre,

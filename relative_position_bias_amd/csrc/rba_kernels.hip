@@ -519,8 +519,9 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
     return halves_max(M);
 }
 
-template <int DV, int NW>
+template <int DV, bool WIN>
 __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
+    constexpr int NW = WIN ? 8 : 4;  // waves that issue the K/V copies
     __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 K1[BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 V0[BS * DV];
@@ -620,13 +621,21 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             const int js = kb * BS + 32 * sub;
-            if (js + 32 <= js_end && rel_active(js + 32))
-                rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, js + 32, A.R, rel_inside(js + 32), lane);
-            if (ok_cur && !masked_all(C, js, A.W)) {
+            // The next subtile's bias is requested before this subtile's
+            // scores, or (with a window, where every subtile has bias) after
+            // them: the wait for this subtile's bias drains every load issued
+            // before it, so a request placed ahead of it would be waited for
+            // too.
+            auto prefetch_rel = [&]() {
+                if (js + 32 <= js_end && rel_active(js + 32))
+                    rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, js + 32, A.R, rel_inside(js + 32), lane);
+            };
+            auto scores = [&](float(&x)[16]) {
                 const f32x16 s = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
-                float x[16];
-                float M = sm_scores_rv(C, s, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W),
-                                       js, A.W, A.R, A.c1, lane, x);
+                return sm_scores_rv(C, s, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W), js,
+                                    A.W, A.R, A.c1, lane, x);
+            };
+            auto finish = [&](float M, float(&x)[16]) {
                 if (__any(!C.m_set || sm_trigger(C, M))) {
                     if (__any(!C.m_set)) sm_init_ref(C, M, x);
                     if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
@@ -638,6 +647,21 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
 #pragma unroll
                     for (int dt = 0; dt < DV / 32; ++dt)
                         C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * c) * DV, vbo[dt], DV), pb[c], C.O[dt]);
+                }
+            };
+            const bool computed = ok_cur && !masked_all(C, js, A.W);
+            if constexpr (WIN) {
+                float x[16];
+                float M = -INFINITY;
+                if (computed) M = scores(x);
+                prefetch_rel();
+                if (computed) finish(M, x);
+            } else {
+                prefetch_rel();
+                if (computed) {
+                    float x[16];
+                    const float M = scores(x);
+                    finish(M, x);
                 }
             }
         }
@@ -1248,12 +1272,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
-    if (a.W > 0) {  // windowed: every subtile streams bias, all waves issue the K/V copies
-        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, 8>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<64, 8>), g, blk, 0, s, a);
+    if (a.W > 0) {  // windowed: every subtile streams bias
+        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<64, true>), g, blk, 0, s, a);
     } else {
-        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, 4>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<64, 4>), g, blk, 0, s, a);
+        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<64, false>), g, blk, 0, s, a);
     }
     return hipGetLastError();
 }
