@@ -50,6 +50,8 @@ PREFILL_GRID = [
     ([97, 5, 64], [31, 400, 0], 12, 2, 128, 40, 37),  # G = 6, odd window
     ([64], [4096], 4, 1, 64, 1024, 0),         # chunk over a long context
     ([333], [0], 2, 2, 128, 8, 1),             # window of 1: only the key itself
+    ([0, 50, 0, 70], [10, 20, 5, 0], 8, 2, 128, 64, 0),  # sequences with no new tokens
+    ([64, 128], [64, 0], 8, 2, 64, 128, 0),    # tile-aligned, no ragged tail
 ]
 
 
@@ -99,6 +101,7 @@ DECODE_GRID = [
     (5, 2, [128, 256, 384, 4000, 77], 8, 8, 64, 64, 128, 64),   # G = 1, aliased pool
     (2, 4, [300, 1100], 16, 4, 128, 256, 0, None),      # G * n_q = 16: the 16-column kernel's limit
     (2, 5, [300, 1100], 16, 4, 64, 256, 0, None),       # G * n_q = 20: the 32-column kernel, one group
+    (2, 4, [4, 1000], 16, 4, 128, 256, 0, None),        # a sequence holding only its n_q new tokens
 ]
 
 
@@ -141,7 +144,7 @@ def test_split_count_invariance():
     say("split invariance")
     b = W.make_decode(5, 2, 2, 32, 8, 128, 1024, 0, seq_lens=[3000, 7000]).to(DEV)
     outs = []
-    for s in (1, 2, 0, 55):
+    for s in (1, 2, 0, 55, 300):  # 300: more splits than blocks (empty splits) and than one combine pass
         o, l = run_decode(b, num_splits=s, want_lse=True)
         outs.append((o.clone(), l.clone()))
     vmax = float(b.v_cache.float().nan_to_num(0).abs().max())
