@@ -89,7 +89,7 @@ def algorithmic(b, kind):
     flops = pairs * b.Hq * (2 * DQK + 2 * b.dv)
     rows = b.rows
     q_bytes = rows * b.Hq * DQK * 2
-    kv_bytes = keys * b.Hkv * (DQK + b.dv) * 2
+    kv_bytes = keys * b.Hkv * (DQK + b.dv) * (1 if getattr(b, "kv_fp8", False) else 2)  # e4m3: 1 byte
     rel_bytes = biased * b.Hq * 4
     out_bytes = rows * b.Hq * b.dv * 4
     blocks = sum((L + 127) // 128 for L in seq_lens)

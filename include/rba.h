@@ -224,6 +224,35 @@ int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q
                        int32_t num_splits, const void* workspace, size_t workspace_bytes,
                        float* out, float* lse, void* stream);
 
+/*
+ * Decode over an FP8 KV cache. Source: "vLLM TML Inkling Support", section
+ * "Future Roadmap" (FP8 for global attention, to cut the KV-cache cost). The
+ * pages give no format or scale convention; this library reads:
+ *   k_cache, v_cache  device e4m3 (OCP FP8: 1 sign, 4 exponent bits with bias
+ *                7, 3 mantissa bits, no infinities, S.1111.111 = NaN), one
+ *                byte per element, same [num_blocks, Hkv, 128, 128] and
+ *                [num_blocks, Hkv, 128, dv] layouts as the bf16 cache
+ *   k_scale, v_scale  per-tensor dequantization scales: the key / value used is
+ *                the e4m3 value times the scale (finite, > 0)
+ * Everything else (arguments, workspace, split plan, combine, errors) is as
+ * rba_decode / rba_decode_split; the output is attention over the dequantized
+ * K/V. rba_decode_fp8 = rba_decode_split_fp8 + rba_decode_combine.
+ */
+int rba_decode_fp8(const rba_attn_params* params,
+                   const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                   float k_scale, float v_scale, const float* rel, const int32_t* seq_lens,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                   void* workspace, size_t workspace_bytes,
+                   float* out, float* lse, void* stream);
+
+int rba_decode_split_fp8(const rba_attn_params* params,
+                         const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                         float k_scale, float v_scale, const float* rel, const int32_t* seq_lens,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

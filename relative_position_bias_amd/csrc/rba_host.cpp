@@ -253,6 +253,8 @@ rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void*
     a.R = p->rel_extent;
     a.W = p->window;
     a.c1 = (float)((double)p->scale * 1.4426950408889634);
+    a.v_scale = 1.0f;
+    a.kv8 = 0;
     a.n_q = n_q;
     a.n_cg = (int32_t)ceil_div((int64_t)G * n_q, 32);
     a.splits = splits;
@@ -411,6 +413,64 @@ int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache
     if (rc || nothing) return rc;
     rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
                                     max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+static int check_kv_scales(float k_scale, float v_scale) {
+    if (!(k_scale > 0.f && k_scale < INFINITY) || !(v_scale > 0.f && v_scale < INFINITY))
+        return fail(RBA_ERR_SHAPE, "k_scale %g / v_scale %g must be finite and > 0", (double)k_scale,
+                    (double)v_scale);
+    return RBA_OK;
+}
+
+static rba::DecodeArgs fp8_args(rba::DecodeArgs a, const rba_attn_params* p, float k_scale, float v_scale) {
+    a.c1 = (float)((double)p->scale * (double)k_scale * 1.4426950408889634);
+    a.v_scale = v_scale;
+    a.kv8 = 1;
+    return a;
+}
+
+int rba_decode_split_fp8(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                         int32_t num_blocks, float k_scale, float v_scale, const float* rel,
+                         const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (num_splits < 1) return fail(RBA_ERR_SHAPE, "rba_decode_split_fp8 needs a resolved num_splits >= 1");
+    int rc = check_kv_scales(k_scale, v_scale);
+    if (rc) return rc;
+    bool nothing;
+    int32_t splits = 0;
+    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                         batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, nullptr, nullptr, false,
+                         &splits, &nothing);
+    if (rc || nothing) return rc;
+    rba::DecodeArgs a = fp8_args(decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                             max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace),
+                                 params, k_scale, v_scale);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return ok();
+}
+
+int rba_decode_fp8(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                   int32_t num_blocks, float k_scale, float v_scale, const float* rel, const int32_t* seq_lens,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
+                   int32_t max_seq_len, int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                   float* lse, void* stream) {
+    int rc = check_kv_scales(k_scale, v_scale);
+    if (rc) return rc;
+    bool nothing;
+    int32_t splits = 0;
+    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                         batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, out, lse, true, &splits,
+                         &nothing);
+    if (rc || nothing) return rc;
+    rba::DecodeArgs a = fp8_args(decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                             max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace),
+                                 params, k_scale, v_scale);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
     if (e != hipSuccess) return hip_fail(e, "decode split launch");

@@ -40,7 +40,9 @@ struct DecodeArgs {
     float* part_lse;          // fp32 [batch * n_q, Hq, splits]
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
-    float c1;
+    float c1;                 // scale * log2(e), times the K dequantization scale for e4m3 K/V
+    float v_scale;            // V dequantization scale (1 for bf16 K/V)
+    int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3 (OCP FP8, one byte)
     int32_t n_q, n_cg, splits, bps;   // column groups of 32 (head, token) pairs; blocks per split
 };
 

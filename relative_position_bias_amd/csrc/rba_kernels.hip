@@ -56,6 +56,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rba_internal.h"
 
 namespace rba {
@@ -732,8 +734,116 @@ __device__ __forceinline__ void store_v_sub(__bf16* Vw, const VSub<DV>& v, int l
     }
 }
 
+// e4m3 (OCP FP8) K/V. A cache element is one byte; gfx950's
+// v_cvt_pk_f32_fp8 decodes e4m3 to fp32, and every e4m3 value (3 mantissa
+// bits, exponents 2^-9 .. 2^8) is exact in bf16, so the MFMAs see exactly the
+// stored values. The dequantization scales are folded into the score scale
+// (K) and the split outputs (V).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 values (lowest address first) as 8 bf16.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(const u32x2& w) {
+    const uint32_t w0 = w[0], w1 = w[1];
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    bf16x8 r;
+    r[0] = (__bf16)a[0];
+    r[1] = (__bf16)a[1];
+    r[2] = (__bf16)b[0];
+    r[3] = (__bf16)b[1];
+    r[4] = (__bf16)c[0];
+    r[5] = (__bf16)c[1];
+    r[6] = (__bf16)d[0];
+    r[7] = (__bf16)d[1];
+    return r;
+}
+
+// load_k_sub for e4m3 K: the same elements, 8 bytes per operand.
+__device__ __forceinline__ void load_k_sub8(u32x2 (&kr)[8], const uint8_t* kblk, int sub, int lane) {
+    const uint8_t* row = kblk + (32 * sub + perm32(lane & 31)) * DQK + 8 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kr[st] = *reinterpret_cast<const u32x2*>(row + 16 * st);
+}
+
+// V subtile of e4m3 V as 16-byte pieces of 16 values; widened to bf16 when
+// stored to LDS (same LDS layout as store_v_sub).
 template <int DV>
+struct VSub8 {
+    static constexpr int PIECES = 32 * (DV / 16) / 64;  // per lane
+    u32x4 r[PIECES];
+};
+
+template <int DV>
+__device__ __forceinline__ void load_v_sub8(VSub8<DV>& v, const uint8_t* vblk, int sub, int nvalid, int lane) {
+#pragma unroll
+    for (int k = 0; k < VSub8<DV>::PIECES; ++k) {
+        const int p = lane + 64 * k;
+        const int key = 32 * sub + p / (DV / 16), c = p % (DV / 16);
+        v.r[k] = key < nvalid ? *reinterpret_cast<const u32x4*>(vblk + key * DV + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int DV>
+__device__ __forceinline__ void store_v_sub8(__bf16* Vw, const VSub8<DV>& v, int lane) {
+#pragma unroll
+    for (int k = 0; k < VSub8<DV>::PIECES; ++k) {
+        const int p = lane + 64 * k;
+        __bf16* dst = Vw + (p / (DV / 16)) * vrow<DV>() + 16 * (p % (DV / 16));
+        const u32x4 w = v.r[k];
+        *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16(u32x2{w[0], w[1]});
+        *reinterpret_cast<bf16x8*>(dst + 8) = fp8x8_to_bf16(u32x2{w[2], w[3]});
+    }
+}
+
+// K/V element type of the decode kernels: bf16 (KV8 = false) or e4m3.
+template <bool KV8>
+struct Kv {
+    typedef bf16x8 KReg;
+    template <int DV>
+    using VRegs = VSub<DV>;
+    static constexpr int ESZ = 2;
+    __device__ static bf16x8 op(const KReg& k) { return k; }
+    __device__ static void k_sub(KReg (&kr)[8], const char* kblk, int sub, int lane) {
+        load_k_sub(kr, reinterpret_cast<const uint16_t*>(kblk), sub, lane);
+    }
+    template <int DV>
+    __device__ static void v_load(VRegs<DV>& v, const char* vblk, int sub, int nvalid, int lane) {
+        load_v_sub<DV>(v, reinterpret_cast<const uint16_t*>(vblk), sub, nvalid, lane);
+    }
+    template <int DV>
+    __device__ static void v_store(__bf16* Vw, const VRegs<DV>& v, int lane) {
+        store_v_sub<DV>(Vw, v, lane);
+    }
+};
+
+template <>
+struct Kv<true> {
+    typedef u32x2 KReg;
+    template <int DV>
+    using VRegs = VSub8<DV>;
+    static constexpr int ESZ = 1;
+    __device__ static bf16x8 op(const KReg& k) { return fp8x8_to_bf16(k); }
+    __device__ static void k_sub(KReg (&kr)[8], const char* kblk, int sub, int lane) {
+        load_k_sub8(kr, reinterpret_cast<const uint8_t*>(kblk), sub, lane);
+    }
+    template <int DV>
+    __device__ static void v_load(VRegs<DV>& v, const char* vblk, int sub, int nvalid, int lane) {
+        load_v_sub8<DV>(v, reinterpret_cast<const uint8_t*>(vblk), sub, nvalid, lane);
+    }
+    template <int DV>
+    __device__ static void v_store(__bf16* Vw, const VRegs<DV>& v, int lane) {
+        store_v_sub8<DV>(Vw, v, lane);
+    }
+};
+
+template <int DV, bool KV8>
 __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
+    using KV = Kv<KV8>;
+    const char* const kbase = reinterpret_cast<const char*>(A.k);
+    const char* const vbase = reinterpret_cast<const char*>(A.v);
     __shared__ __attribute__((aligned(16))) char smem[DecodeLds<DV>::TOTAL];
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
@@ -797,14 +907,14 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             okk = phys >= 0 && phys < A.num_blocks;
             return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
         };
-        bf16x8 kr[8];
-        VSub<DV> vs;
+        typename KV::KReg kr[8];
+        typename KV::template VRegs<DV> vs;
         bool ok_cur = false;
         if (ka <= kz) {
             const size_t base = block_base(ka, ok_cur);
             if (ok_cur) {
-                load_k_sub(kr, A.k + base * DQK, wid, lane);
-                load_v_sub<DV>(vs, A.v + base * DV, wid, L - ka * BS, lane);
+                KV::k_sub(kr, kbase + base * DQK * KV::ESZ, wid, lane);
+                KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, wid, L - ka * BS, lane);
             }
         }
 #pragma unroll 1
@@ -815,8 +925,8 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             if (!ok_cur) {
                 bad = true;
                 if (ok_next) {
-                    load_k_sub(kr, A.k + base_next * DQK, wid, lane);
-                    load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+                    KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, wid, lane);
+                    KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, wid, L - (kb + 1) * BS, lane);
                 }
                 ok_cur = ok_next;
                 continue;
@@ -824,10 +934,13 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             const bool brel = bias_on(C, js, A.R);
             RelRegs rr;
             if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
-            store_v_sub<DV>(Vw, vs, lane);
-            if (ok_next) load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
-            const f32x16 s = qk_regs(kr, C.qreg);
-            if (ok_next) load_k_sub(kr, A.k + base_next * DQK, wid, lane);
+            KV::template v_store<DV>(Vw, vs, lane);
+            if (ok_next) KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, wid, L - (kb + 1) * BS, lane);
+            bf16x8 kb16[8];
+#pragma unroll
+            for (int st = 0; st < 8; ++st) kb16[st] = KV::op(kr[st]);
+            const f32x16 s = qk_regs(kb16, C.qreg);
+            if (ok_next) KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, wid, lane);
             if (brel) rel_store(Rw, rr, lane);
             __builtin_amdgcn_wave_barrier();
             softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
@@ -845,14 +958,17 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             }
             const size_t base = ((size_t)phys * A.Hkv + g) * BS;
             const bool brel = bias_on(C, js, A.R);
-            bf16x8 kr[8];
-            VSub<DV> vs;
-            load_k_sub(kr, A.k + base * DQK, wid, lane);
-            load_v_sub<DV>(vs, A.v + base * DV, wid, L - kb * BS, lane);
-            store_v_sub<DV>(Vw, vs, lane);
+            typename KV::KReg kr[8];
+            typename KV::template VRegs<DV> vs;
+            KV::k_sub(kr, kbase + base * DQK * KV::ESZ, wid, lane);
+            KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, wid, L - kb * BS, lane);
+            KV::template v_store<DV>(Vw, vs, lane);
             RelRegs rr;
             if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
-            const f32x16 s = qk_regs(kr, C.qreg);
+            bf16x8 kb16[8];
+#pragma unroll
+            for (int st = 0; st < 8; ++st) kb16[st] = KV::op(kr[st]);
+            const f32x16 s = qk_regs(kb16, C.qreg);
             if (brel) rel_store(Rw, rr, lane);
             __builtin_amdgcn_wave_barrier();
             softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
@@ -905,7 +1021,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
         }
         const int ctt = cc / A.G, chl = cc % A.G;
         const long long prow = ((long long)(b * A.n_q + ctt) * A.Hq + (g * A.G + chl)) * A.splits + split;
-        A.part_o[prow * DV + dv] = any_bad ? NAN : (M > -INFINITY ? num / den : 0.f);
+        A.part_o[prow * DV + dv] = any_bad ? NAN : (M > -INFINITY ? num / den * A.v_scale : 0.f);
         if (dv == 0) {
             A.part_lse[prow] = any_bad ? NAN : (M > -INFINITY ? (M + __log2f(den)) * LN2 : -INFINITY);
         }
@@ -953,6 +1069,16 @@ __device__ __forceinline__ float groups_sum(float v) {
 
 // K operands of one 32-key subtile: kr[2 h + ... ] in order (h, s):
 // lane loads key 32 sub + 8 (m/4) + 4 h + m%4 (m = l & 15), dims 32 s + 8 q.
+__device__ __forceinline__ void load_k16(u32x2 (&kr)[8], const uint8_t* kblk, int sub, int lane) {
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint8_t* row = kblk + (32 * sub + 8 * (m >> 2) + 4 * h + (m & 3)) * DQK + 8 * q;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kr[4 * h + st] = *reinterpret_cast<const u32x2*>(row + 32 * st);
+    }
+}
+
 __device__ __forceinline__ void load_k16(bf16x8 (&kr)[8], const uint16_t* kblk, int sub, int lane) {
     const int m = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -987,8 +1113,12 @@ struct Decode16Lds {
     static constexpr int TOTAL = (4 * V_BYTES > MERGE) ? 4 * V_BYTES : MERGE;
 };
 
-template <int DV>
+template <int DV, bool KV8>
 __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs A) {
+    using KV = Kv<KV8>;
+    typedef typename std::conditional<KV8, uint8_t, uint16_t>::type KElem;
+    const KElem* const kel = reinterpret_cast<const KElem*>(A.k);
+    const KElem* const vel = reinterpret_cast<const KElem*>(A.v);
     __shared__ __attribute__((aligned(16))) char smem[Decode16Lds<DV>::TOTAL];
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1053,14 +1183,14 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
         return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
     };
 
-    bf16x8 kr[8];
-    VSub<DV> vs;
+    typename KV::KReg kr[8];
+    typename KV::template VRegs<DV> vs;
     bool ok_cur = false;
     if (ka <= kz) {
         const size_t base = block_base(ka, ok_cur);
         if (ok_cur) {
-            load_k16(kr, A.k + base * DQK, wid, lane);
-            load_v_sub<DV>(vs, A.v + base * DV, wid, L - ka * BS, lane);
+            load_k16(kr, kel + base * DQK, wid, lane);
+            KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base * DV), wid, L - ka * BS, lane);
         }
     }
 #pragma unroll 1
@@ -1071,23 +1201,26 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
         if (!ok_cur) {
             bad = true;
             if (ok_next) {
-                load_k16(kr, A.k + base_next * DQK, wid, lane);
-                load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+                load_k16(kr, kel + base_next * DQK, wid, lane);
+                KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base_next * DV), wid,
+                                        L - (kb + 1) * BS, lane);
             }
             ok_cur = ok_next;
             continue;
         }
-        store_v_sub<DV>(Vw, vs, lane);
-        if (ok_next) load_v_sub<DV>(vs, A.v + base_next * DV, wid, L - (kb + 1) * BS, lane);
+        KV::template v_store<DV>(Vw, vs, lane);
+        if (ok_next)
+            KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base_next * DV), wid, L - (kb + 1) * BS,
+                                    lane);
         // S^T halves
         f32x4v S[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             S[hh] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int st = 0; st < 4; ++st) S[hh] = mfma16(kr[4 * hh + st], qreg[st], S[hh]);
+            for (int st = 0; st < 4; ++st) S[hh] = mfma16(KV::op(kr[4 * hh + st]), qreg[st], S[hh]);
         }
-        if (ok_next) load_k16(kr, A.k + base_next * DQK, wid, lane);
+        if (ok_next) load_k16(kr, kel + base_next * DQK, wid, lane);
         // logits (log2 units, relative to the reference), bias, masks
         const bool brel = w_lo - (js + 31) < A.R;
         const bool nmask = phantom || (js + 31 > w_lo) || (A.W > 0 && w_hi - js >= A.W);
@@ -1182,7 +1315,7 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
         }
         const int ctt = col / A.G, chl = col % A.G;
         const long long prow = ((long long)(b * A.n_q + ctt) * A.Hq + (g * A.G + chl)) * A.splits + split;
-        A.part_o[prow * DV + dv] = any_bad ? NAN : (Mx > -INFINITY ? num / den : 0.f);
+        A.part_o[prow * DV + dv] = any_bad ? NAN : (Mx > -INFINITY ? num / den * A.v_scale : 0.f);
         if (dv == 0) {
             A.part_lse[prow] = any_bad ? NAN : (Mx > -INFINITY ? (Mx + __log2f(den)) * LN2 : -INFINITY);
         }
@@ -1285,18 +1418,24 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.Hkv * a.n_cg * a.splits;
     if (grid <= 0) return hipSuccess;
+    const dim3 g((unsigned)grid), blk(256);
+    const bool kv8 = a.kv8 != 0;
     if (a.G * a.n_q <= 16) {  // one 16-column group (n_cg == 1)
         if (dv == 128) {
-            hipLaunchKernelGGL(decode16_split_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+            if (kv8) hipLaunchKernelGGL((decode16_split_kernel<128, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((decode16_split_kernel<128, false>), g, blk, 0, s, a);
         } else {
-            hipLaunchKernelGGL(decode16_split_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
+            if (kv8) hipLaunchKernelGGL((decode16_split_kernel<64, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((decode16_split_kernel<64, false>), g, blk, 0, s, a);
         }
         return hipGetLastError();
     }
     if (dv == 128) {
-        hipLaunchKernelGGL(decode_split_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        if (kv8) hipLaunchKernelGGL((decode_split_kernel<128, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((decode_split_kernel<128, false>), g, blk, 0, s, a);
     } else {
-        hipLaunchKernelGGL(decode_split_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        if (kv8) hipLaunchKernelGGL((decode_split_kernel<64, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((decode_split_kernel<64, false>), g, blk, 0, s, a);
     }
     return hipGetLastError();
 }

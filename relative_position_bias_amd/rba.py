@@ -67,6 +67,12 @@ _SIGNATURES = {
                                         _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
     "rba_decode_combine": (ctypes.c_int, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _ptr, _size, _ptr,
                                           _ptr, _ptr]),
+    "rba_decode_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
+                                      ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _ptr,
+                                      _size, _ptr, _ptr, _ptr]),
+    "rba_decode_split_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
+                                            ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
+                                            _ptr, _size, _ptr]),
 }
 
 _lib = None
@@ -185,13 +191,20 @@ def _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q, window
     return params(Hq, Hkv, dv, R, window, scale, dqk, bs), batch, rows, Hq, dv, nb
 
 
+def _kv8(t: torch.Tensor) -> torch.Tensor:
+    """An e4m3 cache as raw bytes (uint8 or torch.float8_e4m3fn accepted)."""
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
 def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
            max_seq_len: int, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           want_lse: bool = False, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+           want_lse: bool = False, kv_scales: Optional[Tuple[float, float]] = None,
+           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_decode (split-KV + combine). q [batch*n_q, Hq, 128] bf16; rel
     [batch*n_q, Hq, R] fp32. `workspace` (uint8, on the GPU) is allocated with
-    torch if not given."""
+    torch if not given. With kv_scales = (k_scale, v_scale) the caches are
+    e4m3 bytes and rba_decode_fp8 runs."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
     L = lib()
@@ -202,6 +215,16 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    if kv_scales is not None:
+        _check(L.rba_decode_fp8(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(_kv8(k_cache), torch.uint8, "k_cache"),
+            _dev(_kv8(v_cache), torch.uint8, "v_cache"), nb, float(kv_scales[0]), float(kv_scales[1]),
+            _dev(rel, torch.float32, "rel"), _dev(seq_lens, torch.int32, "seq_lens"),
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q,
+            int(max_seq_len), int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream)))
+        return out, lse
     _check(L.rba_decode(
         ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
         _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
@@ -213,10 +236,21 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
 
 
 def decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
-                 max_seq_len: int, num_splits: int, workspace: torch.Tensor, stream=None) -> None:
-    """rba_decode_split: partial outputs of every split into `workspace`."""
+                 max_seq_len: int, num_splits: int, workspace: torch.Tensor,
+                 kv_scales: Optional[Tuple[float, float]] = None, stream=None) -> None:
+    """rba_decode_split: partial outputs of every split into `workspace`
+    (rba_decode_split_fp8 with kv_scales, e4m3 caches)."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
+    if kv_scales is not None:
+        _check(lib().rba_decode_split_fp8(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(_kv8(k_cache), torch.uint8, "k_cache"),
+            _dev(_kv8(v_cache), torch.uint8, "v_cache"), nb, float(kv_scales[0]), float(kv_scales[1]),
+            _dev(rel, torch.float32, "rel"), _dev(seq_lens, torch.int32, "seq_lens"),
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q,
+            int(max_seq_len), int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _stream(stream)))
+        return
     _check(lib().rba_decode_split(
         ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
         _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),

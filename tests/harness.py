@@ -34,8 +34,14 @@ def oracle_batch(batch: workloads.Batch, rows=None):
                 continue
         nb = (L + workloads.BLOCK - 1) // workloads.BLOCK
         blocks = batch.block_tables[b, :nb].long()
-        k = oracle.unpage(batch.k_cache[blocks].double().numpy(), [list(range(nb))], [L])
-        v = oracle.unpage(batch.v_cache[blocks].double().numpy(), [list(range(nb))], [L])
+        if batch.kv_fp8:  # e4m3 bytes times the per-tensor scale
+            kb = oracle.e4m3_to_float(batch.k_cache[blocks].numpy()) * batch.k_scale
+            vb = oracle.e4m3_to_float(batch.v_cache[blocks].numpy()) * batch.v_scale
+        else:
+            kb = batch.k_cache[blocks].double().numpy()
+            vb = batch.v_cache[blocks].double().numpy()
+        k = oracle.unpage(kb, [list(range(nb))], [L])
+        v = oracle.unpage(vb, [list(range(nb))], [L])
         if local is None:
             o, l = oracle.attend(batch.q[start:start + ql].double().numpy(), k, v,
                                  batch.rel[start:start + ql].double().numpy(), [ql], [L], **kw)
@@ -60,6 +66,8 @@ def run_prefill(b: workloads.Batch, want_lse=False, **kw):
 
 
 def run_decode(b: workloads.Batch, num_splits=0, want_lse=False, **kw):
+    if b.kv_fp8:
+        kw.setdefault("kv_scales", (b.k_scale, b.v_scale))
     return rba.decode(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
                       window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
                       want_lse=want_lse, **kw)

@@ -19,7 +19,7 @@ P = 0x10000          # a fake, 16-byte aligned device address
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rba_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rba_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -198,3 +198,16 @@ def test_errors_are_thread_local():
     t.join()
     assert seen == [""]
     assert rba.last_error() != ""
+
+
+def test_fp8_decode_rejects_bad_scales():
+    """Scale checks run before any HIP call (no device needed)."""
+    lib = rba.lib()
+    p = dprm()
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        rc = lib.rba_decode_fp8(ctypes.byref(p), P, P, P, 2560, ks, vs, P, P, P, 1024, 16, 1, 131072, 0, P,
+                                1 << 30, P, None, None)
+        assert rc == rba.RBA_ERR_SHAPE, (ks, vs, rc)
+        rc = lib.rba_decode_split_fp8(ctypes.byref(p), P, P, P, 2560, ks, vs, P, P, P, 1024, 16, 1, 131072, 8,
+                                      P, 1 << 30, None)
+        assert rc == rba.RBA_ERR_SHAPE, (ks, vs, rc)

@@ -134,6 +134,55 @@ def test_verify_decode_workloads(name):
 
 
 # ---------------------------------------------------------------------------
+# decode over e4m3 (FP8) K/V caches
+# ---------------------------------------------------------------------------
+FP8_GRID = [
+    # (batch, n_q, seq_lens, Hq, Hkv, dv, R, W)
+    (3, 1, [129, 1000, 5000], 32, 8, 128, 1024, 0),   # G * n_q = 4: the 16-column kernel
+    (2, 4, [300, 1100], 16, 4, 64, 256, 0),            # 16-column kernel, dv 64
+    (2, 4, [700, 4096], 64, 8, 64, 1024, 0),           # G * n_q = 32: 32-column kernel with prefetch
+    (2, 8, [900, 2000], 48, 8, 128, 512, 0),           # 48 columns, dv 128: two groups, no prefetch
+    (4, 3, [3, 250, 520, 1300], 16, 4, 128, 256, 300), # window; a sequence shorter than a block
+]
+
+
+@pytest.mark.parametrize("case", FP8_GRID, ids=lambda c: f"B{c[0]}nq{c[1]}H{c[3]}/{c[4]}dv{c[5]}W{c[7]}")
+@pytest.mark.parametrize("splits", [1, 0])
+def test_decode_fp8_small(case, splits):
+    batch, n_q, lens, Hq, Hkv, dv, R, Wn = case
+    say(f"decode fp8 {case} splits={splits}")
+    b = W.make_decode(31, batch, n_q, Hq, Hkv, dv, R, Wn, seq_lens=lens, kv_fp8=True)
+    gpu_vs_oracle(b, what=f"fp8 {case} s{splits}", num_splits=splits)
+
+
+def test_decode_fp8_equals_bf16_on_dequantized_cache():
+    """Same attention as the bf16 path over caches holding the dequantized
+    values (exact in bf16 for the workloads' scales). Only the place where the
+    scales are applied differs: K's is folded into the score scale, V's into
+    the split outputs, so the two agree to fp32 rounding."""
+    say("fp8 vs bf16 on the dequantized cache")
+    b8 = W.make_decode(33, 3, 2, 32, 8, 128, 1024, 0, seq_lens=[500, 3000, 9000], kv_fp8=True)
+    k = (b8.k_cache.view(torch.float8_e4m3fn).float() * b8.k_scale).to(torch.bfloat16)
+    v = (b8.v_cache.view(torch.float8_e4m3fn).float() * b8.v_scale).to(torch.bfloat16)
+    bb = W.Batch(**{**b8.__dict__, "k_cache": k, "v_cache": v, "kv_fp8": False, "k_scale": 1.0,
+                    "v_scale": 1.0})
+    o8, l8 = run_decode(b8.to(DEV), want_lse=True)
+    ob, lb = run_decode(bb.to(DEV), want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o8).all()
+    assert float((o8 - ob).abs().max()) <= 4e-3 and float((o8 - ob).abs().mean()) <= 1e-4
+    assert float((l8 - lb).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["paged_decode_16x8k_128k_disjoint_fp8", "verify_decode_b1_100k_fp8",
+                                  "verify_decode_b8_100k_fp8"])
+def test_fp8_decode_workloads(name):
+    say(name)
+    _, mx, mean = gpu_vs_oracle(W.build(name), what=name)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+# ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------
 def test_split_count_invariance():

@@ -449,3 +449,45 @@ def test_mutants_are_caught(name, monkeypatch):
                 caught = True
                 break
         assert caught, f"mutant {name} passed the brute-force pin"
+
+
+# ---------------------------------------------------------------------------
+# e4m3 decoding of the FP8-KV decode's caches
+# ---------------------------------------------------------------------------
+def test_e4m3_decode_hand_values():
+    """Values fixed by the OCP FP8 e4m3 definition (bias 7, 3 mantissa bits,
+    subnormals below 2^-6, S.1111.111 = NaN, no infinities)."""
+    table = {0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x30: 0.5, 0xB8: -1.0, 0x77: 240.0}
+    codes = np.array(list(table), dtype=np.uint8)
+    got = oracle.e4m3_to_float(codes)
+    assert np.array_equal(got, np.array(list(table.values())))
+    assert np.signbit(oracle.e4m3_to_float(np.array([0x80], dtype=np.uint8)))[0]  # -0
+    assert np.isnan(oracle.e4m3_to_float(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    """All 256 codes against an independent decoder (torch.float8_e4m3fn)."""
+    codes = np.arange(256, dtype=np.uint8)
+    a = oracle.e4m3_to_float(codes)
+    b = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    ok = ~np.isnan(a)
+    assert np.array_equal(a[ok], b[ok]) and np.array_equal(np.signbit(a[ok]), np.signbit(b[ok]))
+
+
+def test_fp8_decode_oracle_is_bf16_oracle_on_dequantized_cache():
+    """The oracle of an e4m3 batch equals the oracle of the same batch with the
+    caches replaced by their dequantized values (exact in bf16 for these
+    scales), i.e. the FP8 path changes only where K/V come from."""
+    import workloads as W
+    from harness import oracle_batch
+    b8 = W.make_decode(7, 2, 2, 8, 2, 64, 128, 0, seq_lens=[130, 300], kv_fp8=True)
+    k = torch.from_numpy(oracle.e4m3_to_float(b8.k_cache.numpy()) * b8.k_scale)
+    v = torch.from_numpy(oracle.e4m3_to_float(b8.v_cache.numpy()) * b8.v_scale)
+    assert torch.equal(k.to(torch.bfloat16).double().nan_to_num(7.0), k.nan_to_num(7.0))  # exact in bf16
+    bb = W.Batch(**{**b8.__dict__, "k_cache": k.to(torch.bfloat16), "v_cache": v.to(torch.bfloat16),
+                    "kv_fp8": False, "k_scale": 1.0, "v_scale": 1.0})
+    o8, l8 = oracle_batch(b8)
+    ob, lb = oracle_batch(bb)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)

@@ -11,6 +11,10 @@ are identical on every machine:
   rel: 0.5 * standard normal in fp32.
   Pool blocks that no table references, and slots past a sequence's length in
   its last block, are filled with bf16 NaN so that stray reads show up.
+  e4m3 (OCP FP8) K/V caches, for the FP8-KV decode: the bf16 draws above
+  divided by the per-tensor scale (K_SCALE_FP8, V_SCALE_FP8) and rounded to
+  e4m3 by torch (round to nearest even; |x / scale| stays far below 448), kept
+  as raw bytes; NaN slots stay NaN.
 
 The workloads stand in for the pages' traffic (8K-token prompts, 32K-256K
 agentic sessions, a 100K-context decode at batch 1, 16 sequences in a
@@ -28,6 +32,8 @@ BLOCK = 128
 HEAD_DIM = 128
 _CHUNK = 1 << 24
 BF16_NAN = 0x7FC0
+K_SCALE_FP8 = 0.0625     # per-tensor dequantization scales of the e4m3 workloads
+V_SCALE_FP8 = 0.09375
 
 # Named workloads (sizes as the pages and the task describe them).
 WORKLOADS = {
@@ -46,6 +52,9 @@ WORKLOADS = {
     "verify_decode_b8_100k": dict(kind="decode", batch=8, seq_len=100000, n_q=4, Hq=64, Hkv=8, dv=64,
                                   R=1024, W=0, pool_blocks=None),
 }
+# The decode workloads again over e4m3 K/V caches.
+for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k", "verify_decode_b8_100k"):
+    WORKLOADS[_name + "_fp8"] = dict(WORKLOADS[_name], kv_fp8=True)
 
 
 @dataclass
@@ -69,6 +78,9 @@ class Batch:
     q_lens: List[int] = field(default_factory=list)
     max_q_len: int = 0
     max_seq_len: int = 0
+    kv_fp8: bool = False                  # k_cache / v_cache hold e4m3 bytes (uint8)
+    k_scale: float = 1.0                  # dequantization scales of e4m3 caches
+    v_scale: float = 1.0
 
     def to(self, device) -> "Batch":
         kw = {}
@@ -115,6 +127,16 @@ def _poison(k_cache, v_cache, tables: List[List[int]], seq_lens: List[int]) -> N
         vv[blk, :, s:, :] = BF16_NAN
 
 
+def _to_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """x / scale rounded to e4m3 by torch, as raw bytes (chunked)."""
+    out = torch.empty(x.shape, dtype=torch.uint8)
+    src, dst = x.view(-1), out.view(-1)
+    for s in range(0, src.numel(), _CHUNK):
+        e = min(src.numel(), s + _CHUNK)
+        dst[s:e] = (src[s:e].float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
+
+
 def _tables_tensor(tables: List[List[int]], max_blocks: int) -> torch.Tensor:
     t = torch.full((len(tables), max_blocks), -1, dtype=torch.int32)
     for b, tab in enumerate(tables):
@@ -158,7 +180,7 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
 
 def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: int, W: int,
                 seq_lens: Optional[List[int]] = None, len_range=None, seq_len: Optional[int] = None,
-                pool_blocks: Optional[int] = None, scale: Optional[float] = None) -> Batch:
+                pool_blocks: Optional[int] = None, scale: Optional[float] = None, kv_fp8: bool = False) -> Batch:
     """`batch` sequences decoding n_q tokens each. Lengths: explicit, one fixed
     `seq_len`, or uniform integers in `len_range` (inclusive). With
     pool_blocks=None every sequence gets its own blocks (one global
@@ -191,12 +213,17 @@ def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: 
         for n in nblk:
             tables.append(torch.randperm(num_blocks, generator=gen)[:n].tolist())
     _poison(k_cache, v_cache, tables, seq_lens)
+    kw = {}
+    if kv_fp8:
+        k_cache = _to_e4m3(k_cache, K_SCALE_FP8)
+        v_cache = _to_e4m3(v_cache, V_SCALE_FP8)
+        kw = dict(kv_fp8=True, k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
     return Batch(kind="decode", Hq=Hq, Hkv=Hkv, dv=dv, R=R, W=W,
                  scale=scale if scale is not None else HEAD_DIM ** -0.5,
                  q=q, k_cache=k_cache, v_cache=v_cache, rel=rel,
                  seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                  block_tables=_tables_tensor(tables, max(nblk)), n_q=n_q,
-                 q_lens=[n_q] * batch, max_q_len=n_q, max_seq_len=max(seq_lens))
+                 q_lens=[n_q] * batch, max_q_len=n_q, max_seq_len=max(seq_lens), **kw)
 
 
 def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
