@@ -39,7 +39,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         i64, dbl, P = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.rba_oracle_attend.argtypes = [i64, P, P, i64, i64, i64, i64, i64, i64, dbl,
-                                          P, P, P, P, P, i64, P, P]
+                                          P, P, P, P, P, P, P, i64, P, P]
         lib.rba_oracle_attend.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -68,7 +68,7 @@ def _f64(a):
 
 
 def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
-           rows=None, out=None, lse=None):
+           rows=None, out=None, lse=None, sink=None, gate=None):
     """Relative-bias GQA attention, float64, over contiguous K/V.
 
     q    [total_q, Hq, dqk]      rows of all sequences packed in order
@@ -78,6 +78,9 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
     q_lens, seq_lens  per-sequence query rows and key count (q_len <= seq_len;
                       the queries are the last q_len positions)
     rows  optional iterable of global query rows to compute (others stay NaN)
+    sink, gate  optional [total_q, Hq] logits of the gated-attention output
+                (a sink in the softmax normaliser with zero value; a sigmoid
+                factor on the output); see oracle.c
     Returns (out [total_q, Hq, dv], lse [total_q, Hq]) as float64.
     """
     lib = _load()
@@ -95,6 +98,14 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
         out = np.full((total_q, Hq, dv), np.nan)
     if lse is None:
         lse = np.full((total_q, Hq), np.nan)
+    if sink is not None:
+        sink = _f64(sink)
+        if sink.shape != (total_q, Hq):
+            raise ValueError("sink must be [total_q, Hq]")
+    if gate is not None:
+        gate = _f64(gate)
+        if gate.shape != (total_q, Hq):
+            raise ValueError("gate must be [total_q, Hq]")
     rows_arr = None
     if rows is not None:
         rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int64))
@@ -102,6 +113,7 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
         len(q_lens), q_lens.ctypes.data, seq_lens.ctypes.data,
         Hq, Hkv, dqk, dv, int(rel_extent), int(window), float(scale),
         q.ctypes.data, k.ctypes.data, v.ctypes.data, rel.ctypes.data,
+        sink.ctypes.data if sink is not None else None, gate.ctypes.data if gate is not None else None,
         rows_arr.ctypes.data if rows_arr is not None else None,
         len(rows_arr) if rows_arr is not None else 0,
         out.ctypes.data, lse.ctypes.data)

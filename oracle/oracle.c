@@ -16,6 +16,11 @@
  *     bias(d)    =  rel[t,h,d]  for 0 <= d < R,  0 for d >= R
  *     out[t,h,:] =  sum_j softmax(x)_j * V_b[j,g,:]
  *     lse[t,h]   =  log sum_j exp(x_j)
+ *   Optional gated-attention outputs (sink, gate may each be NULL):
+ *     with a sink logit s = sink[t,h] the softmax set is {x_j} plus s, whose
+ *     value vector is zero:  out = sum_j exp(x_j) V_j / (sum_j exp(x_j) + exp(s)),
+ *     lse = log(sum_j exp(x_j) + exp(s));
+ *     with a gate logit a = gate[t,h] the output is scaled by 1 / (1 + exp(-a)).
  *
  * Sources (the pages, not code):
  *  - "Inkling-Small on Gaudi 2", section "Why it needed a port": the relative
@@ -36,6 +41,13 @@
  *  - The pages do not say what the bias is for distances at or beyond the
  *    relative extent; this oracle uses 0 there (the reading the library
  *    documents as well).
+ *  - "Inkling 2 Small on vLLM: Day-0 Support", section on the model
+ *    architecture (table row on the attention output, and the paragraph on
+ *    the Inkling backbone and recent advances): each head's output gets a
+ *    sigmoid gate, paired with a per-token attention sink. No formula is
+ *    given; the reading above (a per-(token, head) sink logit in the softmax
+ *    normaliser with a zero value, and a per-(token, head) sigmoid factor on
+ *    the output) is this oracle's and the library's.
  *
  * Layouts (all contiguous, row-major, float64):
  *   q    [total_q, Hq, dqk]     rows of all sequences packed; sequence b owns
@@ -46,6 +58,7 @@
  *   rel  [total_q, Hq, R]
  *   out  [total_q, Hq, dv]
  *   lse  [total_q, Hq]          (may be NULL)
+ *   sink, gate [total_q, Hq]    (each may be NULL)
  * The query rows of sequence b are its last q_len_b positions:
  *   i = seq_len_b - q_len_b + (t - q_start_b).
  *
@@ -72,7 +85,7 @@ int rba_oracle_attend(int64_t batch, const int64_t* q_lens, const int64_t* seq_l
                       int64_t Hq, int64_t Hkv, int64_t dqk, int64_t dv,
                       int64_t R, int64_t W, double scale,
                       const double* q, const double* k, const double* v,
-                      const double* rel,
+                      const double* rel, const double* sink, const double* gate,
                       const int64_t* rows, int64_t n_rows,
                       double* out, double* lse) {
     if (batch <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dqk <= 0 || dv <= 0 ||
@@ -122,8 +135,11 @@ int rba_oracle_attend(int64_t batch, const int64_t* q_lens, const int64_t* seq_l
                 x[j - lo] = scale * s + bias;
                 if (x[j - lo] > m) m = x[j - lo];
             }
+            /* the sink logit joins the softmax set (its value is zero) */
+            const double sk = sink ? sink[t * Hq + h] : -INFINITY;
+            if (sk > m) m = sk;
             /* softmax weights and the weighted sum of values */
-            double l = 0.0;
+            double l = sink ? exp(sk - m) : 0.0;
             for (int64_t j = lo; j <= i; ++j) {
                 x[j - lo] = exp(x[j - lo] - m);
                 l += x[j - lo];
@@ -134,6 +150,10 @@ int rba_oracle_attend(int64_t batch, const int64_t* q_lens, const int64_t* seq_l
                 const double p = x[j - lo] / l;
                 const double* vr = v + ((kv_start[b] + j) * Hkv + g) * dv;
                 for (int64_t c = 0; c < dv; ++c) o[c] += p * vr[c];
+            }
+            if (gate) {
+                const double f = 1.0 / (1.0 + exp(-gate[t * Hq + h]));
+                for (int64_t c = 0; c < dv; ++c) o[c] *= f;
             }
             if (lse) lse[t * Hq + h] = m + log(l);
         }

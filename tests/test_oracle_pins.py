@@ -434,7 +434,7 @@ def test_mutants_are_caught(name, monkeypatch):
         lib = ctypes.CDLL(so)
         i64, dbl, P = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.rba_oracle_attend.argtypes = [i64, P, P, i64, i64, i64, i64, i64, i64, dbl,
-                                          P, P, P, P, P, i64, P, P]
+                                          P, P, P, P, P, P, P, i64, P, P]
         lib.rba_oracle_attend.restype = ctypes.c_int
         monkeypatch.setattr(oracle, "_lib", lib)
         caught = False
@@ -491,3 +491,96 @@ def test_fp8_decode_oracle_is_bf16_oracle_on_dequantized_cache():
     o8, l8 = oracle_batch(b8)
     ob, lb = oracle_batch(bb)
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
+# ---------------------------------------------------------------------------
+# gated-attention output: per-(token, head) sink logit and sigmoid gate
+# ---------------------------------------------------------------------------
+def _gated_case(seed=5):
+    rng = np.random.default_rng(seed)
+    c = make_case(rng, [7, 12], [20, 12], 4, 2, 16, 8, 6)
+    tq = int(sum(c["q_lens"]))
+    sink = rng.standard_normal((tq, 4)) * 2.0
+    gate = rng.standard_normal((tq, 4)) * 2.0
+    return c, sink, gate
+
+
+def test_gated_sink_minus_inf_and_gate_plus_inf_are_the_plain_attention():
+    c, _, _ = _gated_case()
+    o, l = run_oracle(c, 6, 0, 0.25)
+    tq = o.shape[0]
+    og, lg = oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"], rel_extent=6, window=0,
+                           scale=0.25, sink=np.full((tq, 4), -np.inf), gate=np.full((tq, 4), np.inf))
+    assert np.array_equal(o, og) and np.array_equal(l, lg)
+
+
+def test_gated_gate_zero_halves_the_output():
+    c, sink, _ = _gated_case()
+    o, l = oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"], rel_extent=6, window=0,
+                         scale=0.25, sink=sink)
+    og, lg = oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"], rel_extent=6, window=0,
+                           scale=0.25, sink=sink, gate=np.zeros_like(sink))
+    assert np.array_equal(og, 0.5 * o) and np.array_equal(lg, l)
+
+
+def test_gated_sink_closed_form_uniform_scores():
+    """q = k = 0, rel = 0: every visible logit is 0, so with n visible keys
+    out = sum_j v_j / (n + e^s) and lse = log(n + e^s); the gate multiplies by
+    1 / (1 + e^-a)."""
+    c, sink, gate = _gated_case(9)
+    c = dict(c, q=np.zeros_like(c["q"]), k=np.zeros_like(c["k"]), rel=np.zeros_like(c["rel"]))
+    W = 5
+    o, l = oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"], rel_extent=6, window=W,
+                         scale=0.25, sink=sink, gate=gate)
+    t = 0
+    k0 = 0
+    for Lq, L in zip(c["q_lens"], c["seq_lens"]):
+        for r in range(int(Lq)):
+            i = int(L) - int(Lq) + r
+            lo = max(0, i - W + 1)
+            for h in range(4):
+                g = h // 2
+                n = i - lo + 1
+                vs = c["v"][k0 + lo:k0 + i + 1, g].sum(axis=0)
+                den = n + math.exp(sink[t, h])
+                want = vs / den / (1.0 + math.exp(-gate[t, h]))
+                assert np.allclose(o[t, h], want, rtol=1e-13, atol=1e-13)
+                assert abs(l[t, h] - math.log(den)) <= 1e-13
+            t += 1
+        k0 += int(L)
+
+
+def test_gated_large_sink_takes_all_the_weight():
+    c, sink, _ = _gated_case()
+    big = np.full_like(sink, 800.0)
+    o, l = oracle.attend(c["q"], c["k"], c["v"], c["rel"], c["q_lens"], c["seq_lens"], rel_extent=6, window=0,
+                         scale=0.25, sink=big)
+    assert np.abs(o).max() < 1e-300 and np.allclose(l, 800.0, rtol=0, atol=1e-12)
+
+
+GATED_MUTANTS = {
+    "sink_dropped_from_sum": ("double l = sink ? exp(sk - m) : 0.0;", "double l = 0.0;"),
+    "gate_sign": ("exp(-gate[t * Hq + h])", "exp(gate[t * Hq + h])"),
+    "sink_value_not_zero": ("const double p = x[j - lo] / l;", "const double p = x[j - lo] / (l - (sink ? exp(sk - m) : 0.0));"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(GATED_MUTANTS))
+def test_gated_mutants_are_caught(name, monkeypatch):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    old, new = GATED_MUTANTS[name]
+    assert src.count(old) == 1, name
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "m.c")
+        open(path, "w").write(src.replace(old, new))
+        so = os.path.join(d, "libm.so")
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", path, "-o", so, "-lm"], check=True)
+        lib = ctypes.CDLL(so)
+        i64, dbl, P = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.rba_oracle_attend.argtypes = [i64, P, P, i64, i64, i64, i64, i64, i64, dbl,
+                                          P, P, P, P, P, P, P, i64, P, P]
+        lib.rba_oracle_attend.restype = ctypes.c_int
+        monkeypatch.setattr(oracle, "_lib", lib)
+        with pytest.raises(AssertionError):
+            test_gated_sink_closed_form_uniform_scores()
