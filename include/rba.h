@@ -225,6 +225,48 @@ int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q
                        float* out, float* lse, void* stream);
 
 /*
+ * Gated attention output (Inkling 2 Small). Source: "Inkling 2 Small on vLLM:
+ * Day-0 Support", model-architecture section (the attention-output row of the
+ * comparison table, and the paragraph on the Inkling backbone and recent
+ * advances: a sigmoid gate on each head's output, paired with a per-token
+ * attention sink). No formula is given; this library reads:
+ *   sink  device fp32 [rows, Hq] or NULL: a logit (natural-log units, finite
+ *         or -inf) per (query token, head) that joins the softmax normaliser
+ *         with a zero value vector:
+ *           out = sum_j e^(x_j) V_j / (sum_j e^(x_j) + e^sink),
+ *           lse = log(sum_j e^(x_j) + e^sink)
+ *   gate  device fp32 [rows, Hq] or NULL: out is multiplied by 1 / (1 + e^-gate)
+ *         (lse is unchanged)
+ * rows = total_q (prefill) or batch * n_q (decode). With both NULL each call
+ * is exactly its ungated counterpart. sink and gate must be 4-byte aligned
+ * (RBA_ERR_UNSUPPORTED otherwise); every other argument and error is as in
+ * rba_prefill / rba_decode / rba_decode_combine. The decode's split stage is
+ * unchanged (rba_decode_split or rba_decode_split_fp8); the sink and gate are
+ * applied by the combine.
+ */
+int rba_prefill_gated(const rba_attn_params* params,
+                      const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                      const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                      const float* sink, const float* gate,
+                      float* out, float* lse, void* stream);
+
+int rba_decode_gated(const rba_attn_params* params,
+                     const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                     const float* rel, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes,
+                     const float* sink, const float* gate,
+                     float* out, float* lse, void* stream);
+
+int rba_decode_combine_gated(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                             int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                             const float* sink, const float* gate,
+                             float* out, float* lse, void* stream);
+
+/*
  * Decode over an FP8 KV cache. Source: "vLLM TML Inkling Support", section
  * "Future Roadmap" (FP8 for global attention, to cut the KV-cache cost). The
  * pages give no format or scale convention; this library reads:

@@ -283,10 +283,12 @@ int rba_validate_prefill(const rba_attn_params* params, const void* q, const voi
                             max_blocks_per_seq, batch, max_q_len, max_seq_len, out, nullptr, &nothing);
 }
 
-int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
-                int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
-                const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
-                int32_t max_seq_len, float* out, float* lse, void* stream) {
+int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                      int32_t max_seq_len, const float* sink, const float* gate, float* out, float* lse,
+                      void* stream) {
+    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
     bool nothing;
     int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
                               max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing);
@@ -302,6 +304,8 @@ int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cach
     a.tables = block_tables;
     a.out = out;
     a.lse = lse;
+    a.sink = sink;
+    a.gate = gate;
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.batch = batch;
@@ -318,6 +322,14 @@ int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cach
     hipError_t e = rba::launch_prefill(a, params->head_dim_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
+}
+
+int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                int32_t max_seq_len, float* out, float* lse, void* stream) {
+    return rba_prefill_gated(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, max_q_len, max_seq_len, nullptr, nullptr, out, lse, stream);
 }
 
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,
@@ -373,8 +385,10 @@ int rba_decode_split(const rba_attn_params* params, const void* q, const void* k
     return ok();
 }
 
-int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q, int32_t num_splits,
-                       const void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+int rba_decode_combine_gated(const rba_attn_params* params, int32_t batch, int32_t n_q, int32_t num_splits,
+                             const void* workspace, size_t workspace_bytes, const float* sink, const float* gate,
+                             float* out, float* lse, void* stream) {
+    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
     int rc = check_params(params);
     if (rc) return rc;
     if (batch < 0 || n_q < 1) return fail(RBA_ERR_SHAPE, "batch %d / n_q %d invalid", batch, n_q);
@@ -394,11 +408,19 @@ int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q
     a.part_lse = static_cast<const float*>(workspace) + (size_t)pairs * num_splits * params->head_dim_v;
     a.out = out;
     a.lse = lse;
+    a.sink = sink;
+    a.gate = gate;
     a.pairs = (int32_t)pairs;
     a.splits = num_splits;
     hipError_t e = rba::launch_combine(a, params->head_dim_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();
+}
+
+int rba_decode_combine(const rba_attn_params* params, int32_t batch, int32_t n_q, int32_t num_splits,
+                       const void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+    return rba_decode_combine_gated(params, batch, n_q, num_splits, workspace, workspace_bytes, nullptr, nullptr,
+                                    out, lse, stream);
 }
 
 int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -417,6 +439,27 @@ int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache
     hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
     if (e != hipSuccess) return hip_fail(e, "decode split launch");
     return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int rba_decode_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                     int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, const float* sink,
+                     const float* gate, float* out, float* lse, void* stream) {
+    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
+    bool nothing;
+    int32_t splits = 0;
+    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                             workspace_bytes, out, lse, true, &splits, &nothing);
+    if (rc || nothing) return rc;
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return rba_decode_combine_gated(params, batch, n_q, splits, workspace, workspace_bytes, sink, gate, out, lse,
+                                    stream);
 }
 
 static int check_kv_scales(float k_scale, float v_scale) {

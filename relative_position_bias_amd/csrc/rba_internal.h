@@ -19,6 +19,8 @@ struct PrefillArgs {
     const int32_t* tables;    // [batch, max_blocks]
     float* out;               // fp32 [total_q, Hq, dv]
     float* lse;               // fp32 [total_q, Hq] or null
+    const float* sink;        // fp32 [total_q, Hq] sink logits, or null (no sink)
+    const float* gate;        // fp32 [total_q, Hq] gate logits, or null (no gate)
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
     float c1;                 // scale * log2(e)
@@ -51,6 +53,8 @@ struct CombineArgs {
     const float* part_lse;
     float* out;
     float* lse;
+    const float* sink;        // fp32 [batch * n_q, Hq] sink logits, or null
+    const float* gate;        // fp32 [batch * n_q, Hq] gate logits, or null
     int32_t pairs;            // batch * n_q * Hq
     int32_t splits;
 };

@@ -339,11 +339,22 @@ __device__ __forceinline__ void init_acc(Cols<DV>& C) {
 }
 
 // Write the normalised output (and lse) of a finished wave: lane holds
-// dv = 32 dt + 8 q4 + 4 hh + k of column lane & 31.
+// dv = 32 dt + 8 q4 + 4 hh + k of column lane & 31. `sink` (natural-log
+// units, -inf for none) joins the softmax normaliser with a zero value;
+// `gate` scales the output by 1 / (1 + e^-gate) (+inf for none).
 template <int DV>
-__device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float* lse, bool bad, int lane) {
-    const float l_tot = C.l_sum + xor32(C.l_sum);
-    const float inv = bad ? NAN : 1.f / l_tot;
+__device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float* lse, bool bad, float sink,
+                                          float gate, int lane) {
+    float l_tot = C.l_sum + xor32(C.l_sum);
+    float mref = C.m_ref, o_fac = 1.f;
+    if (sink > -INFINITY) {  // move the reference to max(reference, sink) and add the sink's term
+        const float s2 = sink * LOG2E, mn = fmaxf(mref, s2);
+        o_fac = __builtin_amdgcn_exp2f(mref - mn);
+        l_tot = l_tot * o_fac + __builtin_amdgcn_exp2f(s2 - mn);
+        mref = mn;
+    }
+    const float g = gate < INFINITY ? 1.f / (1.f + __builtin_amdgcn_exp2f(-gate * LOG2E)) : 1.f;
+    const float inv = bad ? NAN : o_fac / l_tot * g;
     const int hh = lane >> 5;
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt) {
@@ -355,7 +366,7 @@ __device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float*
             *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * q4 + 4 * hh) = o;
         }
     }
-    if (lse != nullptr && hh == 0) *lse = bad ? NAN : (C.m_ref + __log2f(l_tot)) * LN2;
+    if (lse != nullptr && hh == 0) *lse = bad ? NAN : (mref + __log2f(l_tot)) * LN2;
 }
 
 // ---------------------------------------------------------------------------
@@ -676,7 +687,8 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     }
 
     if (!wave_active || !real) return;
-    store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, lane);
+    store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
+              A.gate ? A.gate[trow] : INFINITY, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1358,6 +1370,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
     }
 
     float M = fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3]));
+    const float sk = A.sink ? A.sink[pair] : -INFINITY;  // joins the normaliser with a zero value
+    M = fmaxf(M, sk);
     const bool nan_here = (lv[0] != lv[0]) || (lv[1] != lv[1]) || (lv[2] != lv[2]) || (lv[3] != lv[3]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
@@ -1378,6 +1392,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
     if ((tid & 63) == 0) red[1][wid] = den;
     __syncthreads();
     den = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    if (sk > -INFINITY) den += __builtin_amdgcn_exp2f((sk - M) * LOG2E);
 
     float acc = 0.f;
 #pragma unroll
@@ -1393,7 +1408,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
         float tot = part[0][d];
 #pragma unroll
         for (int g2 = 1; g2 < GROUPS; ++g2) tot += part[g2][d];
-        const float inv = nan_seen ? NAN : 1.f / den;
+        const float gt = A.gate ? A.gate[pair] : INFINITY;
+        const float g = gt < INFINITY ? 1.f / (1.f + __builtin_amdgcn_exp2f(-gt * LOG2E)) : 1.f;
+        const float inv = nan_seen ? NAN : g / den;
         A.out[pair * DV + d] = tot * inv;
         if (A.lse != nullptr && d == 0) A.lse[pair] = nan_seen ? NAN : M + logf(den);
     }

@@ -67,6 +67,12 @@ _SIGNATURES = {
                                         _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
     "rba_decode_combine": (ctypes.c_int, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _ptr, _size, _ptr,
                                           _ptr, _ptr]),
+    "rba_prefill_gated": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                         _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr, _ptr, _ptr]),
+    "rba_decode_gated": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                        _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr, _ptr, _ptr, _ptr, _ptr]),
+    "rba_decode_combine_gated": (ctypes.c_int, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _ptr, _size,
+                                                _ptr, _ptr, _ptr, _ptr, _ptr]),
     "rba_decode_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
                                       ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _ptr,
                                       _size, _ptr, _ptr, _ptr]),
@@ -131,14 +137,25 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _opt(t: Optional[torch.Tensor], name: str, shape) -> Optional[int]:
+    """Device pointer of an optional fp32 [rows, Hq] input (sink / gate)."""
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}")
+    return _dev(t, torch.float32, name)
+
+
 def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: int, scale: float,
             max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+            sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill. q [total_q, Hq, 128] bf16; k_cache [nb, Hkv, 128, 128] bf16;
     v_cache [nb, Hkv, 128, dv] bf16; rel [total_q, Hq, R] fp32; cu_q [B+1],
     seq_lens [B], block_tables [B, max_blocks] int32. max_q_len / max_seq_len
-    are host-side bounds (no device read happens here)."""
+    are host-side bounds (no device read happens here). With sink and/or gate
+    (fp32 [total_q, Hq]) rba_prefill_gated runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -153,6 +170,16 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     if lse is None and want_lse:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
+    if sink is not None or gate is not None:
+        _check(lib().rba_prefill_gated(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+            _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
+            int(max_seq_len), _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
+            _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream)))
+        return out, lse
     _check(lib().rba_prefill(
         ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
         _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
@@ -161,6 +188,10 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
         int(max_seq_len), _dev(out, torch.float32, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
     return out, lse
+
+
+def _num_cus(device) -> int:
+    return torch.cuda.get_device_properties(device).multi_processor_count
 
 
 def plan_splits(Hq, Hkv, dv, rel_extent, window, scale, batch, n_q, max_seq_len, num_cus=256) -> int:
@@ -200,11 +231,13 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
            max_seq_len: int, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            want_lse: bool = False, kv_scales: Optional[Tuple[float, float]] = None,
+           sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_decode (split-KV + combine). q [batch*n_q, Hq, 128] bf16; rel
     [batch*n_q, Hq, R] fp32. `workspace` (uint8, on the GPU) is allocated with
     torch if not given. With kv_scales = (k_scale, v_scale) the caches are
-    e4m3 bytes and rba_decode_fp8 runs."""
+    e4m3 bytes and rba_decode_fp8 runs. With sink and/or gate (fp32
+    [batch*n_q, Hq]) the merge is rba_decode_combine_gated."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
     L = lib()
@@ -215,6 +248,28 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    if sink is not None or gate is not None:
+        splits = int(num_splits) or plan_splits(Hq, p.num_heads_kv, dv, p.rel_extent, window, scale, batch, n_q,
+                                                int(max_seq_len), _num_cus(q.device))
+        if kv_scales is not None:
+            decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q=n_q, window=window, scale=scale,
+                         max_seq_len=max_seq_len, num_splits=splits, workspace=workspace, kv_scales=kv_scales,
+                         stream=stream)
+            _check(L.rba_decode_combine_gated(
+                ctypes.byref(p), batch, n_q, splits, _dev(workspace, torch.uint8, "workspace"),
+                workspace.numel(), _opt(sink, "sink", (rows, Hq)), _opt(gate, "gate", (rows, Hq)),
+                _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+                _stream(stream)))
+            return out, lse
+        _check(L.rba_decode_gated(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+            _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+            block_tables.shape[1], batch, n_q, int(max_seq_len), splits,
+            _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _opt(sink, "sink", (rows, Hq)),
+            _opt(gate, "gate", (rows, Hq)), _dev(out, torch.float32, "out"),
+            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+        return out, lse
     if kv_scales is not None:
         _check(L.rba_decode_fp8(
             ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(_kv8(k_cache), torch.uint8, "k_cache"),
@@ -261,9 +316,19 @@ def decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, 
 
 def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, scale: float, batch: int,
                    n_q: int, num_splits: int, workspace: torch.Tensor, out: torch.Tensor,
-                   lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """rba_decode_combine: log-sum-exp merge of the partials in `workspace`."""
+                   lse: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+                   gate: Optional[torch.Tensor] = None, stream=None) -> None:
+    """rba_decode_combine: log-sum-exp merge of the partials in `workspace`
+    (rba_decode_combine_gated with sink and/or gate)."""
     p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    if sink is not None or gate is not None:
+        rows = batch * n_q
+        _check(lib().rba_decode_combine_gated(
+            ctypes.byref(p), batch, n_q, int(num_splits), _dev(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _opt(sink, "sink", (rows, Hq)), _opt(gate, "gate", (rows, Hq)),
+            _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream)))
+        return
     _check(lib().rba_decode_combine(
         ctypes.byref(p), batch, n_q, int(num_splits), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.float32, "out"),

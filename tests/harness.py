@@ -42,9 +42,13 @@ def oracle_batch(batch: workloads.Batch, rows=None):
             vb = batch.v_cache[blocks].double().numpy()
         k = oracle.unpage(kb, [list(range(nb))], [L])
         v = oracle.unpage(vb, [list(range(nb))], [L])
+        def gated(a, b_):
+            return dict(sink=batch.sink[a:b_].double().numpy() if batch.sink is not None else None,
+                        gate=batch.gate[a:b_].double().numpy() if batch.gate is not None else None)
         if local is None:
             o, l = oracle.attend(batch.q[start:start + ql].double().numpy(), k, v,
-                                 batch.rel[start:start + ql].double().numpy(), [ql], [L], **kw)
+                                 batch.rel[start:start + ql].double().numpy(), [ql], [L], **kw,
+                                 **gated(start, start + ql))
             out[start:start + ql] = o
             lse[start:start + ql] = l
         else:
@@ -52,7 +56,7 @@ def oracle_batch(batch: workloads.Batch, rows=None):
                 i = L - ql + r
                 t = start + r
                 o, l = oracle.attend(batch.q[t:t + 1].double().numpy(), k[:i + 1], v[:i + 1],
-                                     batch.rel[t:t + 1].double().numpy(), [1], [i + 1], **kw)
+                                     batch.rel[t:t + 1].double().numpy(), [1], [i + 1], **kw, **gated(t, t + 1))
                 out[t] = o[0]
                 lse[t] = l[0]
         start += ql
@@ -60,6 +64,10 @@ def oracle_batch(batch: workloads.Batch, rows=None):
 
 
 def run_prefill(b: workloads.Batch, want_lse=False, **kw):
+    if b.sink is not None:
+        kw.setdefault("sink", b.sink)
+    if b.gate is not None:
+        kw.setdefault("gate", b.gate)
     return rba.prefill(b.q, b.k_cache, b.v_cache, b.rel, b.cu_q, b.seq_lens, b.block_tables,
                        window=b.W, scale=b.scale, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
                        want_lse=want_lse, **kw)
@@ -68,6 +76,10 @@ def run_prefill(b: workloads.Batch, want_lse=False, **kw):
 def run_decode(b: workloads.Batch, num_splits=0, want_lse=False, **kw):
     if b.kv_fp8:
         kw.setdefault("kv_scales", (b.k_scale, b.v_scale))
+    if b.sink is not None:
+        kw.setdefault("sink", b.sink)
+    if b.gate is not None:
+        kw.setdefault("gate", b.gate)
     return rba.decode(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
                       window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
                       want_lse=want_lse, **kw)

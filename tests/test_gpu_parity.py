@@ -183,6 +183,77 @@ def test_fp8_decode_workloads(name):
 
 
 # ---------------------------------------------------------------------------
+# gated attention output (sink logit + sigmoid gate, Inkling 2 Small)
+# ---------------------------------------------------------------------------
+GATED_PREFILL = [
+    # (q_lens, ctx_lens, Hq, Hkv, dv, R, W)
+    ([200, 77], [0, 300], 48, 8, 128, 1024, 0),    # 6:1 GQA, no window
+    ([130, 64], [1000, 0], 48, 8, 128, 1024, 96),  # window
+    ([97], [31], 8, 2, 64, 128, 0),                # dv 64
+]
+
+
+@pytest.mark.parametrize("case", GATED_PREFILL, ids=lambda c: f"q{c[0]}H{c[2]}/{c[3]}dv{c[4]}W{c[6]}")
+def test_prefill_gated_small(case):
+    q_lens, ctx, Hq, Hkv, dv, R, Wn = case
+    say(f"prefill gated {case}")
+    gpu_vs_oracle(W.make_prefill(41, q_lens, ctx, Hq, Hkv, dv, R, Wn, gated=True), what=f"gated {case}")
+
+
+GATED_DECODE = [
+    # (batch, n_q, seq_lens, Hq, Hkv, dv, R, W, kv_fp8)
+    (2, 8, [900, 3000], 48, 8, 128, 1024, 0, False),   # 48 columns: two 32-column groups
+    (2, 8, [900, 3000], 48, 8, 128, 1024, 0, True),
+    (3, 1, [129, 1000, 5000], 32, 8, 128, 1024, 300, False),  # 16-column kernel, window
+    (2, 4, [700, 2000], 64, 8, 64, 1024, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", GATED_DECODE, ids=lambda c: f"B{c[0]}nq{c[1]}H{c[3]}/{c[4]}W{c[7]}fp8{int(c[8])}")
+@pytest.mark.parametrize("splits", [1, 0])
+def test_decode_gated_small(case, splits):
+    batch, n_q, lens, Hq, Hkv, dv, R, Wn, fp8 = case
+    say(f"decode gated {case} splits={splits}")
+    b = W.make_decode(43, batch, n_q, Hq, Hkv, dv, R, Wn, seq_lens=lens, kv_fp8=fp8, gated=True)
+    gpu_vs_oracle(b, what=f"gated {case} s{splits}", num_splits=splits)
+
+
+def test_gated_without_sink_or_gate_is_the_plain_path():
+    """sink = -inf and gate = +inf everywhere reproduce the ungated calls bitwise."""
+    say("gated, neutral inputs")
+    b = W.make_prefill(45, [150, 40], [60, 0], 16, 4, 128, 256, 0).to(DEV)
+    neg = torch.full((b.rows, b.Hq), -float("inf"), device=DEV)
+    pos = torch.full((b.rows, b.Hq), float("inf"), device=DEV)
+    o1, l1 = run_prefill(b, want_lse=True)
+    o2, l2 = run_prefill(b, want_lse=True, sink=neg, gate=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    d = W.make_decode(45, 2, 2, 16, 4, 128, 256, 0, seq_lens=[300, 2000]).to(DEV)
+    neg = torch.full((d.rows, d.Hq), -float("inf"), device=DEV)
+    pos = torch.full((d.rows, d.Hq), float("inf"), device=DEV)
+    o1, l1 = run_decode(d, num_splits=3, want_lse=True)
+    o2, l2 = run_decode(d, num_splits=3, want_lse=True, sink=neg, gate=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_inkling2_gated_local_prefill_sampled():
+    name = "inkling2_local_prefill_8k_gated"
+    say(name)
+    b = W.build(name)
+    rows = sample_rows(b)
+    _, mx, mean = gpu_vs_oracle(b, rows=rows, what=name)
+    say(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+
+
+def test_inkling2_gated_verify_decode():
+    name = "inkling2_verify_b1_100k_gated"
+    say(name)
+    _, mx, mean = gpu_vs_oracle(W.build(name), what=name)
+    say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+# ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------
 def test_split_count_invariance():

@@ -11,6 +11,8 @@ are identical on every machine:
   rel: 0.5 * standard normal in fp32.
   Pool blocks that no table references, and slots past a sequence's length in
   its last block, are filled with bf16 NaN so that stray reads show up.
+  Gated-attention inputs (Inkling 2 Small), drawn after everything else:
+  sink = 2 * standard normal and gate = 2 * standard normal, fp32 [rows, Hq].
   e4m3 (OCP FP8) K/V caches, for the FP8-KV decode: the bf16 draws above
   divided by the per-tensor scale (K_SCALE_FP8, V_SCALE_FP8) and rounded to
   e4m3 by torch (round to nearest even; |x / scale| stays far below 448), kept
@@ -52,6 +54,13 @@ WORKLOADS = {
     "verify_decode_b8_100k": dict(kind="decode", batch=8, seq_len=100000, n_q=4, Hq=64, Hkv=8, dv=64,
                                   R=1024, W=0, pool_blocks=None),
 }
+# Inkling 2 Small shapes (48 query / 8 KV heads on every layer, window 1024
+# on local layers, 7 draft tokens + 1 verified = 8 verify tokens) with the
+# gated-attention output (sink and gate inputs).
+WORKLOADS["inkling2_local_prefill_8k_gated"] = dict(kind="prefill", q_lens=[8192], ctx_lens=[0], Hq=48, Hkv=8,
+                                                    dv=128, R=1024, W=1024, permute=True, gated=True)
+WORKLOADS["inkling2_verify_b1_100k_gated"] = dict(kind="decode", batch=1, seq_len=100000, n_q=8, Hq=48, Hkv=8,
+                                                  dv=128, R=1024, W=0, pool_blocks=None, gated=True)
 # The decode workloads again over e4m3 K/V caches.
 for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k", "verify_decode_b8_100k"):
     WORKLOADS[_name + "_fp8"] = dict(WORKLOADS[_name], kv_fp8=True)
@@ -78,6 +87,8 @@ class Batch:
     q_lens: List[int] = field(default_factory=list)
     max_q_len: int = 0
     max_seq_len: int = 0
+    sink: Optional[torch.Tensor] = None   # fp32 [rows, Hq] gated-attention sink logits
+    gate: Optional[torch.Tensor] = None   # fp32 [rows, Hq] gated-attention gate logits
     kv_fp8: bool = False                  # k_cache / v_cache hold e4m3 bytes (uint8)
     k_scale: float = 1.0                  # dequantization scales of e4m3 caches
     v_scale: float = 1.0
@@ -127,6 +138,12 @@ def _poison(k_cache, v_cache, tables: List[List[int]], seq_lens: List[int]) -> N
         vv[blk, :, s:, :] = BF16_NAN
 
 
+def _gated(rows: int, Hq: int, gen: torch.Generator) -> dict:
+    sink = _randn_into(torch.empty((rows, Hq), dtype=torch.float32), gen, 2.0)
+    gate = _randn_into(torch.empty((rows, Hq), dtype=torch.float32), gen, 2.0)
+    return dict(sink=sink, gate=gate)
+
+
 def _to_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
     """x / scale rounded to e4m3 by torch, as raw bytes (chunked)."""
     out = torch.empty(x.shape, dtype=torch.uint8)
@@ -146,7 +163,7 @@ def _tables_tensor(tables: List[List[int]], max_blocks: int) -> torch.Tensor:
 
 def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv: int, dv: int, R: int,
                  W: int, permute: bool = True, scale: Optional[float] = None,
-                 extra_blocks: int = 0) -> Batch:
+                 extra_blocks: int = 0, gated: bool = False) -> Batch:
     """Sequences with ctx_lens[b] cached tokens followed by q_lens[b] new ones
     (whose K/V are already in the cache). One pool holds every sequence's
     blocks, disjoint, permuted if `permute`."""
@@ -166,6 +183,7 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
         o += n
     _poison(k_cache, v_cache, tables, seq_lens)
     max_blocks = max(nblk)
+    extra = _gated(total_q, Hq, gen) if gated else {}
     cu = [0]
     for ql in q_lens:
         cu.append(cu[-1] + ql)
@@ -175,12 +193,13 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
                  seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                  block_tables=_tables_tensor(tables, max_blocks),
                  cu_q=torch.tensor(cu, dtype=torch.int32), q_lens=list(q_lens),
-                 max_q_len=max(q_lens), max_seq_len=max(seq_lens))
+                 max_q_len=max(q_lens), max_seq_len=max(seq_lens), **extra)
 
 
 def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: int, W: int,
                 seq_lens: Optional[List[int]] = None, len_range=None, seq_len: Optional[int] = None,
-                pool_blocks: Optional[int] = None, scale: Optional[float] = None, kv_fp8: bool = False) -> Batch:
+                pool_blocks: Optional[int] = None, scale: Optional[float] = None, kv_fp8: bool = False,
+                gated: bool = False) -> Batch:
     """`batch` sequences decoding n_q tokens each. Lengths: explicit, one fixed
     `seq_len`, or uniform integers in `len_range` (inclusive). With
     pool_blocks=None every sequence gets its own blocks (one global
@@ -213,11 +232,11 @@ def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: 
         for n in nblk:
             tables.append(torch.randperm(num_blocks, generator=gen)[:n].tolist())
     _poison(k_cache, v_cache, tables, seq_lens)
-    kw = {}
+    kw = _gated(batch * n_q, Hq, gen) if gated else {}
     if kv_fp8:
         k_cache = _to_e4m3(k_cache, K_SCALE_FP8)
         v_cache = _to_e4m3(v_cache, V_SCALE_FP8)
-        kw = dict(kv_fp8=True, k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
+        kw.update(kv_fp8=True, k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
     return Batch(kind="decode", Hq=Hq, Hkv=Hkv, dv=dv, R=R, W=W,
                  scale=scale if scale is not None else HEAD_DIM ** -0.5,
                  q=q, k_cache=k_cache, v_cache=v_cache, rel=rel,
@@ -237,7 +256,9 @@ def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
                  rel=full.rel[a:b], seq_lens=torch.tensor([b], dtype=torch.int32, device=dev),
                  block_tables=full.block_tables[:, :nb].contiguous(),
                  cu_q=torch.tensor([0, b - a], dtype=torch.int32, device=dev), q_lens=[b - a],
-                 max_q_len=b - a, max_seq_len=b)
+                 max_q_len=b - a, max_seq_len=b,
+                 sink=full.sink[a:b] if full.sink is not None else None,
+                 gate=full.gate[a:b] if full.gate is not None else None)
 
 
 def build(name: str, seed: int = 0) -> Batch:
