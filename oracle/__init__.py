@@ -122,6 +122,34 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
     return out, lse
 
 
+def rel_from_proj(r, proj):
+    """The bias tensor from the R branch: rel = r @ rel_logits_proj.
+
+    "Inkling-Small on Gaudi 2", section "Attention with a relative bias": each
+    layer computes rel as the product of r (the R branch of the fused QKVR
+    projection) with the layer's rel_logits_proj. The pages give neither the
+    width of r nor whether the projection is shared by the heads. Reading
+    taken here: r holds one vector of width d_r per token and query head, and
+    the projection is one [d_r, R] matrix, either shared by every head or one
+    per query head. It is passed in the layout of a linear layer's weight,
+    i.e. transposed: proj[hp, d, c] is the weight from component c of r to
+    the bias at distance d.
+
+    r     [rows, Hq, d_r]
+    proj  [Hp, R, d_r], Hp = 1 (shared) or Hq (head h uses proj[h])
+    Returns float64 [rows, Hq, R].
+    """
+    r, proj = _f64(r), _f64(proj)
+    rows, Hq, d_r = r.shape
+    Hp, R, d_r2 = proj.shape
+    if d_r2 != d_r or Hp not in (1, Hq):
+        raise ValueError("proj must be [1 or Hq, R, d_r]")
+    rel = np.empty((rows, Hq, R))
+    for h in range(Hq):
+        rel[:, h, :] = r[:, h, :] @ proj[h if Hp == Hq else 0].T
+    return rel
+
+
 def unpage(cache, block_tables, seq_lens, block_size=128):
     """Gather a paged cache [num_blocks, H, block_size, d] into contiguous
     per-sequence rows [sum(seq_lens), H, d] (sequence b: logical block n is

@@ -23,6 +23,11 @@ def oracle_batch(batch: workloads.Batch, rows=None):
     lse = np.full((total, batch.Hq), np.nan)
     want = None if rows is None else set(int(r) for r in rows)
     kw = dict(rel_extent=batch.R, window=batch.W, scale=batch.scale)
+
+    def rel_rows(a, b_):
+        if batch.rel is not None:
+            return batch.rel[a:b_].double().numpy()
+        return oracle.rel_from_proj(batch.r[a:b_].double().numpy(), batch.proj.double().numpy())
     start = 0
     for b, ql in enumerate(batch.q_lens):
         L = int(batch.seq_lens[b])
@@ -47,7 +52,7 @@ def oracle_batch(batch: workloads.Batch, rows=None):
                         gate=batch.gate[a:b_].double().numpy() if batch.gate is not None else None)
         if local is None:
             o, l = oracle.attend(batch.q[start:start + ql].double().numpy(), k, v,
-                                 batch.rel[start:start + ql].double().numpy(), [ql], [L], **kw,
+                                 rel_rows(start, start + ql), [ql], [L], **kw,
                                  **gated(start, start + ql))
             out[start:start + ql] = o
             lse[start:start + ql] = l
@@ -56,7 +61,7 @@ def oracle_batch(batch: workloads.Batch, rows=None):
                 i = L - ql + r
                 t = start + r
                 o, l = oracle.attend(batch.q[t:t + 1].double().numpy(), k[:i + 1], v[:i + 1],
-                                     batch.rel[t:t + 1].double().numpy(), [1], [i + 1], **kw, **gated(t, t + 1))
+                                     rel_rows(t, t + 1), [1], [i + 1], **kw, **gated(t, t + 1))
                 out[t] = o[0]
                 lse[t] = l[0]
         start += ql
@@ -68,6 +73,10 @@ def run_prefill(b: workloads.Batch, want_lse=False, **kw):
         kw.setdefault("sink", b.sink)
     if b.gate is not None:
         kw.setdefault("gate", b.gate)
+    if b.r is not None:
+        return rba.prefill_relproj(b.q, b.k_cache, b.v_cache, b.r, b.proj, b.cu_q, b.seq_lens, b.block_tables,
+                                   window=b.W, scale=b.scale, max_q_len=b.max_q_len,
+                                   max_seq_len=b.max_seq_len, want_lse=want_lse, **kw)
     return rba.prefill(b.q, b.k_cache, b.v_cache, b.rel, b.cu_q, b.seq_lens, b.block_tables,
                        window=b.W, scale=b.scale, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
                        want_lse=want_lse, **kw)

@@ -584,3 +584,90 @@ def test_gated_mutants_are_caught(name, monkeypatch):
         monkeypatch.setattr(oracle, "_lib", lib)
         with pytest.raises(AssertionError):
             test_gated_sink_closed_form_uniform_scores()
+
+
+# ----------------------------------------------------------------------------
+# The bias producer rel = r @ rel_logits_proj ("Inkling-Small on Gaudi 2",
+# section "Attention with a relative bias"). Reading: r is [rows, Hq, d_r],
+# the projection [Hp, R, d_r] in linear-weight layout, shared (Hp = 1) or one
+# per query head (Hp = Hq).
+# ----------------------------------------------------------------------------
+
+def _one_hot_case(rows, Hq, d_r, R, Hp):
+    """r rows are scaled one-hot vectors; the weights are 100 hp + 10 d + c.
+    Then rel[t, h, d] = a(t, h) * (100 hp(h) + 10 d + c(t, h)) exactly."""
+    r = np.zeros((rows, Hq, d_r))
+    a = np.zeros((rows, Hq))
+    sel = np.zeros((rows, Hq), dtype=np.int64)
+    for t in range(rows):
+        for h in range(Hq):
+            sel[t, h] = (t + 2 * h + 1) % d_r
+            a[t, h] = t + 1 + 0.5 * h
+            r[t, h, sel[t, h]] = a[t, h]
+    hp = np.arange(Hp).reshape(Hp, 1, 1)
+    d = np.arange(R).reshape(1, R, 1)
+    c = np.arange(d_r).reshape(1, 1, d_r)
+    proj = (100.0 * hp + 10.0 * d + c) * np.ones((Hp, R, d_r))
+    return r, proj, a, sel
+
+
+@pytest.mark.parametrize("d_r,R", [(8, 6), (8, 8), (5, 11)])
+@pytest.mark.parametrize("shared", [False, True])
+def test_relproj_one_hot_selects_the_weight(d_r, R, shared):
+    rows, Hq = 5, 3
+    Hp = 1 if shared else Hq
+    r, proj, a, sel = _one_hot_case(rows, Hq, d_r, R, Hp)
+    rel = oracle.rel_from_proj(r, proj)
+    assert rel.shape == (rows, Hq, R)
+    for t in range(rows):
+        for h in range(Hq):
+            hp = 0 if shared else h
+            want = a[t, h] * (100.0 * hp + 10.0 * np.arange(R) + sel[t, h])
+            np.testing.assert_array_equal(rel[t, h], want)
+
+
+def test_relproj_constant_r_gives_row_sums():
+    # r = c * ones: rel[t, h, d] = c(t, h) * sum_k proj[hp, d, k]; with
+    # proj[hp, d, k] = k + d*d_r + hp the row sum is d_r*(d_r-1)/2 + d_r*(d*d_r + hp).
+    rows, Hq, d_r, R = 4, 2, 6, 7
+    cst = np.array([[1.0, -2.0], [0.5, 3.0], [0.0, 1.0], [-1.5, 0.25]])
+    r = cst[:, :, None] * np.ones((rows, Hq, d_r))
+    k = np.arange(d_r).reshape(1, 1, d_r)
+    d = np.arange(R).reshape(1, R, 1)
+    hp = np.arange(Hq).reshape(Hq, 1, 1)
+    proj = (k + d * d_r + hp) * np.ones((Hq, R, d_r))
+    rel = oracle.rel_from_proj(r, proj)
+    for h in range(Hq):
+        rowsum = d_r * (d_r - 1) / 2 + d_r * (np.arange(R) * d_r + h)
+        np.testing.assert_array_equal(rel[:, h, :], cst[:, h:h + 1] * rowsum)
+
+
+def test_relproj_rejects_bad_head_count():
+    with pytest.raises(ValueError):
+        oracle.rel_from_proj(np.zeros((2, 4, 8)), np.zeros((2, 5, 8)))
+
+
+def _relproj_mutant(kind):
+    def f(r, proj):
+        r, proj = np.asarray(r, dtype=np.float64), np.asarray(proj, dtype=np.float64)
+        rows, Hq, d_r = r.shape
+        Hp = proj.shape[0]
+        rel = np.empty((rows, Hq, proj.shape[1]))
+        for h in range(Hq):
+            hp = h if Hp == Hq else 0
+            if kind == "head_zero":
+                hp = 0
+            elif kind == "head_reversed" and Hp == Hq:
+                hp = Hq - 1 - h
+            w = proj[hp] if kind == "no_transpose" else proj[hp].T
+            rel[:, h, :] = r[:, h, :] @ w
+        return rel
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_transpose", "head_zero", "head_reversed"])
+def test_relproj_mutants_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "rel_from_proj", _relproj_mutant(kind))
+    with pytest.raises(AssertionError):
+        for d_r, R in [(8, 8)]:
+            test_relproj_one_hot_selects_the_weight(d_r, R, shared=False)

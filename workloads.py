@@ -61,6 +61,10 @@ WORKLOADS["inkling2_local_prefill_8k_gated"] = dict(kind="prefill", q_lens=[8192
                                                     dv=128, R=1024, W=1024, permute=True, gated=True)
 WORKLOADS["inkling2_verify_b1_100k_gated"] = dict(kind="decode", batch=1, seq_len=100000, n_q=8, Hq=48, Hkv=8,
                                                   dv=128, R=1024, W=0, pool_blocks=None, gated=True)
+# The prefills with the bias given by its producer, r (width 64 per token and
+# head; the pages do not give the width) and one shared projection.
+WORKLOADS["local_prefill_8k_relproj"] = dict(WORKLOADS["local_prefill_8k"], d_r=64)
+WORKLOADS["global_chunked_prefill_32k_relproj"] = dict(WORKLOADS["global_chunked_prefill_32k"], d_r=64)
 # The decode workloads again over e4m3 K/V caches.
 for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k", "verify_decode_b8_100k"):
     WORKLOADS[_name + "_fp8"] = dict(WORKLOADS[_name], kv_fp8=True)
@@ -79,7 +83,7 @@ class Batch:
     q: torch.Tensor                 # bf16 [rows, Hq, 128]
     k_cache: torch.Tensor           # bf16 [num_blocks, Hkv, 128, 128]
     v_cache: torch.Tensor           # bf16 [num_blocks, Hkv, 128, dv]
-    rel: torch.Tensor               # fp32 [rows, Hq, R]
+    rel: Optional[torch.Tensor]     # fp32 [rows, Hq, R] (None when r / proj give it)
     seq_lens: torch.Tensor          # int32 [B]
     block_tables: torch.Tensor      # int32 [B, max_blocks]
     cu_q: Optional[torch.Tensor] = None   # int32 [B+1] (prefill)
@@ -92,6 +96,8 @@ class Batch:
     kv_fp8: bool = False                  # k_cache / v_cache hold e4m3 bytes (uint8)
     k_scale: float = 1.0                  # dequantization scales of e4m3 caches
     v_scale: float = 1.0
+    r: Optional[torch.Tensor] = None      # bf16 [rows, Hq, d_r] R-branch vectors (rel not given)
+    proj: Optional[torch.Tensor] = None   # bf16 [1 or Hq, R, d_r] rel_logits_proj, linear-weight layout
 
     def to(self, device) -> "Batch":
         kw = {}
@@ -163,10 +169,13 @@ def _tables_tensor(tables: List[List[int]], max_blocks: int) -> torch.Tensor:
 
 def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv: int, dv: int, R: int,
                  W: int, permute: bool = True, scale: Optional[float] = None,
-                 extra_blocks: int = 0, gated: bool = False) -> Batch:
+                 extra_blocks: int = 0, gated: bool = False, d_r: int = 0, proj_heads: int = 1) -> Batch:
     """Sequences with ctx_lens[b] cached tokens followed by q_lens[b] new ones
     (whose K/V are already in the cache). One pool holds every sequence's
-    blocks, disjoint, permuted if `permute`."""
+    blocks, disjoint, permuted if `permute`. With d_r > 0 the bias is given
+    by its producer instead: r ~ N(0, 1) [rows, Hq, d_r] and a projection
+    ~ N(0, 0.25 / d_r) [proj_heads, R, d_r], so that rel = r @ proj^T has the
+    N(0, 0.5^2) entries of the materialised workloads; rel is then None."""
     gen = torch.Generator().manual_seed(seed)
     seq_lens = [c + q for c, q in zip(ctx_lens, q_lens)]
     nblk = [(L + BLOCK - 1) // BLOCK for L in seq_lens]
@@ -175,7 +184,13 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
     q = _bf16((total_q, Hq, HEAD_DIM), gen)
     k_cache = _bf16((num_blocks, Hkv, BLOCK, HEAD_DIM), gen)
     v_cache = _bf16((num_blocks, Hkv, BLOCK, dv), gen)
-    rel = _randn_into(torch.empty((total_q, Hq, R), dtype=torch.float32), gen, 0.5)
+    rel, relproj = None, {}
+    if d_r > 0:
+        relproj["r"] = _bf16((total_q, Hq, d_r), gen)
+        relproj["proj"] = _randn_into(torch.empty((proj_heads, R, d_r), dtype=torch.bfloat16), gen,
+                                      0.5 / d_r ** 0.5)
+    else:
+        rel = _randn_into(torch.empty((total_q, Hq, R), dtype=torch.float32), gen, 0.5)
     order = torch.randperm(num_blocks, generator=gen).tolist() if permute else list(range(num_blocks))
     tables, o = [], 0
     for n in nblk:
@@ -193,7 +208,7 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
                  seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                  block_tables=_tables_tensor(tables, max_blocks),
                  cu_q=torch.tensor(cu, dtype=torch.int32), q_lens=list(q_lens),
-                 max_q_len=max(q_lens), max_seq_len=max(seq_lens), **extra)
+                 max_q_len=max(q_lens), max_seq_len=max(seq_lens), **extra, **relproj)
 
 
 def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: int, W: int,
@@ -253,12 +268,13 @@ def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
     dev = full.q.device
     return Batch(kind="prefill", Hq=full.Hq, Hkv=full.Hkv, dv=full.dv, R=full.R, W=full.W,
                  scale=full.scale, q=full.q[a:b], k_cache=full.k_cache, v_cache=full.v_cache,
-                 rel=full.rel[a:b], seq_lens=torch.tensor([b], dtype=torch.int32, device=dev),
+                 rel=full.rel[a:b] if full.rel is not None else None, seq_lens=torch.tensor([b], dtype=torch.int32, device=dev),
                  block_tables=full.block_tables[:, :nb].contiguous(),
                  cu_q=torch.tensor([0, b - a], dtype=torch.int32, device=dev), q_lens=[b - a],
                  max_q_len=b - a, max_seq_len=b,
                  sink=full.sink[a:b] if full.sink is not None else None,
-                 gate=full.gate[a:b] if full.gate is not None else None)
+                 gate=full.gate[a:b] if full.gate is not None else None,
+                 r=full.r[a:b] if full.r is not None else None, proj=full.proj)
 
 
 def build(name: str, seed: int = 0) -> Batch:
@@ -271,7 +287,8 @@ def build(name: str, seed: int = 0) -> Batch:
     if kind == "chunked":
         total = w.pop("total")
         w.pop("chunk")
-        return make_prefill(seed, [total], [0], w["Hq"], w["Hkv"], w["dv"], w["R"], w["W"])
+        return make_prefill(seed, [total], [0], w["Hq"], w["Hkv"], w["dv"], w["R"], w["W"],
+                            d_r=w.get("d_r", 0), proj_heads=w.get("proj_heads", 1))
     return make_decode(seed, **w)
 
 
