@@ -128,6 +128,38 @@ int rba_prefill(const rba_attn_params* params,
                 int32_t batch, int32_t max_q_len, int32_t max_seq_len,
                 float* out, float* lse, void* stream);
 
+/*
+ * Prefill with the bias produced inside the kernel from its source, instead
+ * of read from a materialised rel tensor. Source: "Inkling-Small on Gaudi 2",
+ * section "Attention with a relative bias" (each layer forms rel as the
+ * product of r, the R branch of the fused QKVR projection, with the layer's
+ * rel_logits_proj, and hands it to the attention call). Reading: r has one
+ * vector of width d_r per token and query head; the projection is one
+ * [d_r, R] matrix shared by all heads or one per query head; the pages give
+ * neither the width nor the sharing.
+ *
+ *   r            device bf16 [total_q, Hq, d_r], rows as q
+ *   rel_proj     device bf16 [proj_heads, R, d_r], the projection in a linear
+ *                layer's weight layout: element (hp, d, c) multiplies r[..., c]
+ *                into the bias at distance d. Head h uses hp = h when
+ *                proj_heads == Hq, hp = 0 when proj_heads == 1.
+ *   d_r          must be 64 (RBA_ERR_UNSUPPORTED otherwise)
+ *   proj_heads   1 or Hq (RBA_ERR_SHAPE otherwise)
+ *   sink, gate   as rba_prefill_gated (NULL: not applied)
+ *   all other arguments as rba_prefill. The bias of distance d is
+ *   sum_c r[t, h, c] * rel_proj[hp, d, c] (products exact, fp32 sum) for
+ *   0 <= d < R and 0 beyond. r and rel_proj must be 16-byte aligned.
+ * Errors: as rba_prefill.
+ */
+int rba_prefill_relproj(const rba_attn_params* params,
+                        const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                        const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                        const int32_t* cu_q, const int32_t* seq_lens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                        const float* sink, const float* gate,
+                        float* out, float* lse, void* stream);
+
 /* Host-only argument check of rba_prefill (no HIP call; same return codes). */
 int rba_validate_prefill(const rba_attn_params* params,
                          const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,

@@ -156,11 +156,13 @@ size_t ws_bytes(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t sp
     return pairs * (size_t)splits * ((size_t)p->head_dim_v + 1) * sizeof(float);
 }
 
+// `rel` is the bias source the call reads (rel, or r for the in-kernel
+// producer), named `rel_name` in messages.
 int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cache, const void* v_cache,
-                     int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                     int32_t num_blocks, const void* rel, const int32_t* cu_q, const int32_t* seq_lens,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch,
                      int32_t max_q_len, int32_t max_seq_len, const float* out, const float* lse,
-                     bool* nothing) {
+                     bool* nothing, const char* rel_name = "rel") {
     *nothing = false;
     int rc = check_params(p);
     if (rc) return rc;
@@ -172,12 +174,12 @@ int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cach
         *nothing = true;
         return ok();
     }
-    if (q == nullptr || rel == nullptr || out == nullptr) return fail(RBA_ERR_NULL, "q/rel/out is NULL");
+    if (q == nullptr || rel == nullptr || out == nullptr) return fail(RBA_ERR_NULL, "q/%s/out is NULL", rel_name);
     if (cu_q == nullptr || seq_lens == nullptr) return fail(RBA_ERR_NULL, "cu_q/seq_lens is NULL");
     rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
     if (rc) return rc;
     if (!aligned16(q) || !aligned16(rel) || !aligned16(out))
-        return fail(RBA_ERR_UNSUPPORTED, "q/rel/out must be 16-byte aligned");
+        return fail(RBA_ERR_UNSUPPORTED, "q/%s/out must be 16-byte aligned", rel_name);
     if (!aligned4(cu_q) || !aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
         return fail(RBA_ERR_UNSUPPORTED, "cu_q/seq_lens/lse must be 4-byte aligned");
     const int G = p->num_heads_q / p->num_heads_kv;
@@ -299,6 +301,9 @@ int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* 
     a.k = static_cast<const uint16_t*>(k_cache);
     a.v = static_cast<const uint16_t*>(v_cache);
     a.rel = rel;
+    a.r = nullptr;
+    a.proj = nullptr;
+    a.proj_heads = 0;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;
     a.tables = block_tables;
@@ -330,6 +335,55 @@ int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cach
                 int32_t max_seq_len, float* out, float* lse, void* stream) {
     return rba_prefill_gated(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
                              max_blocks_per_seq, batch, max_q_len, max_seq_len, nullptr, nullptr, out, lse, stream);
+}
+
+int rba_prefill_relproj(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t num_blocks, const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                        const float* sink, const float* gate, float* out, float* lse, void* stream) {
+    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
+    bool nothing;
+    int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
+                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r");
+    if (rc || nothing) return rc;
+    if (d_r != 64) return fail(RBA_ERR_UNSUPPORTED, "d_r %d: only 64 is supported", d_r);
+    if (proj_heads != 1 && proj_heads != params->num_heads_q)
+        return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, params->num_heads_q);
+    if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
+    if (!aligned16(rel_proj)) return fail(RBA_ERR_UNSUPPORTED, "rel_proj must be 16-byte aligned");
+    rba::PrefillArgs a;
+    const int G = params->num_heads_q / params->num_heads_kv;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.rel = nullptr;
+    a.r = static_cast<const uint16_t*>(r);
+    a.proj = static_cast<const uint16_t*>(rel_proj);
+    a.proj_heads = proj_heads;
+    a.cu_q = cu_q;
+    a.seq_lens = seq_lens;
+    a.tables = block_tables;
+    a.out = out;
+    a.lse = lse;
+    a.sink = sink;
+    a.gate = gate;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.batch = batch;
+    a.Hq = params->num_heads_q;
+    a.Hkv = params->num_heads_kv;
+    a.G = G;
+    a.R = params->rel_extent;
+    a.W = params->window;
+    a.c1 = (float)((double)params->scale * 1.4426950408889634);
+    a.hpw = prefill_hpw(G);
+    a.QT = 32 * (8 / a.hpw);
+    a.n_qt = (int32_t)ceil_div(max_q_len, a.QT);
+    a.n_hc = G / a.hpw;
+    hipError_t e = rba::launch_prefill_relproj(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
 }
 
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,

@@ -21,6 +21,9 @@ struct PrefillArgs {
     float* lse;               // fp32 [total_q, Hq] or null
     const float* sink;        // fp32 [total_q, Hq] sink logits, or null (no sink)
     const float* gate;        // fp32 [total_q, Hq] gate logits, or null (no gate)
+    const uint16_t* r;        // bf16 [total_q, Hq, 64] R-branch vectors (bias made in the kernel), or null
+    const uint16_t* proj;     // bf16 [proj_heads, R, 64] rel_logits_proj (linear-weight layout)
+    int32_t proj_heads;       // 1 (shared) or Hq
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
     float c1;                 // scale * log2(e)
@@ -60,6 +63,7 @@ struct CombineArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s);
+hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s);
 

@@ -53,6 +53,7 @@
 //     that, with workgroups dealt round-robin to the 8 XCDs, all workgroups of
 //     one KV head (which share its K/V) land on the same XCD and its L2.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -427,13 +428,14 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds) {
 // NW = 4 the early waves issue all copies there, which balances the pair when
 // the score/softmax chain dominates (no window). With a window every subtile
 // also streams its bias from HBM and spreading the copies over all 8 waves
-// is better.
-template <int DV, int NW>
+// is better. ROWS (128 or 64) rows are copied, from kblk / vblk on: a whole
+// block or half of one, in the same per-row layout.
+template <int DV, int NW, int ROWS = BS>
 __device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* kblk, const uint16_t* vblk,
                                        int nvalid, int wid, int lane) {
     if (wid >= NW) return;
 #pragma unroll
-    for (int i = 0; i < 32 / NW; ++i) {
+    for (int i = 0; i < ROWS / (4 * NW); ++i) {
         const int grp = wid + NW * i;  // 1 KB group: K rows 4 grp .. 4 grp + 3
         const int r = 4 * grp + (lane >> 4);
         const int key = (r & ~31) | perm32(r & 31);
@@ -442,7 +444,7 @@ __device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* k
     }
     constexpr int VCH = DV / 8, RPG = 64 / VCH;  // 16-byte chunks per V row, V rows per group
 #pragma unroll
-    for (int i = 0; i < DV / (4 * NW); ++i) {
+    for (int i = 0; i < ROWS / (RPG * NW); ++i) {
         const int grp = wid + NW * i;
         const int r = RPG * grp + lane / VCH;
         const int p = lane % VCH;  // physical chunk; its logical chunk undoes the group rotation
@@ -684,6 +686,277 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
         if (++kb > kb_hi) break;
         step(K1, V1, K0, V0, kb);
         if (++kb > kb_hi) break;
+    }
+
+    if (!wave_active || !real) return;
+    store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
+              A.gate ? A.gate[trow] : INFINITY, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill with the bias produced in the kernel (rel = r @ rel_logits_proj)
+//
+// Instead of reading rel [rows, Hq, R] from HBM, each wave computes the bias
+// its 32 columns need from r (64 values per column, held as an MFMA operand)
+// and the projection (rows of 64 values per distance, read from L2). The
+// wave's columns are 32 consecutive positions w_lo + n of one head, so for
+// the 32 keys js .. js + 31 of a subtile column n needs the distances
+// (w_lo - js) + n - 31 .. (w_lo - js) + n: 63 distinct distances across the
+// wave, sheared by n. Per subtile the wave computes a band
+// T(js)[rho, n] = r_n . proj[(w_lo - js) - 32 + rho] for rho = 0..31 with four
+// 32x32x16 MFMAs and stores it into a per-column ring of 64 distances that
+// also holds T(js - 32) (the distances (w_lo - js) .. + 31). The shear is
+// undone on the way out: each lane reads its 16 bias values as two runs of 8
+// consecutive ring entries starting at a lane-dependent slot. Ring slot of
+// distance d at subtile js: (d - (w_lo - js) + 32 + 32 par(js)) mod 64,
+// par(js) = (js / 32) mod 2; T(js) occupies slots 32 par .. 32 par + 31; slots
+// 0..7 are duplicated at 64..71 so that no run wraps.
+//
+// The ring (32 x 76 floats per wave, 76 KiB for 8 waves) does not fit beside
+// double-buffered whole K/V blocks, so K/V move in half blocks of 64 keys
+// (two subtiles per barrier).
+// ---------------------------------------------------------------------------
+constexpr int DR = 64;       // width of r
+constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
+
+template <int DV, bool WIN>
+__global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
+    constexpr int NW = 8;   // every wave issues copies
+    constexpr int HB = 64;  // keys per K/V stage (half a block)
+    constexpr int SPB = BS / HB;
+    __shared__ __attribute__((aligned(16))) __bf16 K0[HB * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 K1[HB * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 V0[HB * DV];
+    __shared__ __attribute__((aligned(16))) __bf16 V1[HB * DV];
+    __shared__ __attribute__((aligned(16))) float ring_all[8 * 32 * RSTRIDE];
+
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
+    const int hh = lane >> 5;
+    int id = blockIdx.x;
+    const int g = id % A.Hkv;
+    id /= A.Hkv;
+    const int b = id % A.batch;
+    id /= A.batch;
+    const int hc = id % A.n_hc;
+    id /= A.n_hc;
+    const int qt = A.n_qt - 1 - id;  // heavy (late) tiles first
+
+    const int q_start = A.cu_q[b];
+    const int q_len = A.cu_q[b + 1] - q_start;
+    const int L = A.seq_lens[b];
+    const int q0 = qt * A.QT;
+    if (q0 >= q_len) return;  // uniform over the workgroup
+    const int ctx = L - q_len;
+
+    const int hl = hc * A.hpw + wid % A.hpw;
+    const int h = g * A.G + hl;
+    const int qa = q0 + (wid / A.hpw) * 32;
+    const int qb = min(qa + 32, q_len) - 1;
+    const bool wave_active = qa < q_len;
+    const int r = qa + n;
+    const bool real = r < q_len;
+    const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
+
+    Cols<DV> C;
+    C.pos = real ? ctx + r : -1;
+    C.relrow = nullptr;
+    C.w_lo = ctx + qa;
+    C.w_hi = ctx + qb;
+    C.phantom = qb < qa + 31;
+    const uint16_t* proj = A.proj + (size_t)(A.proj_heads == A.Hq ? h : 0) * A.R * DR;
+    float* ring = ring_all + wid * 32 * RSTRIDE + n * RSTRIDE;  // this lane's column
+
+    const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
+    const int s_lo = (A.W > 0 ? max(0, i_lo - A.W + 1) : 0) / HB;
+    const int s_hi = i_hi / HB;
+    const int js_lo = s_lo * HB;
+    const int kb_lo = s_lo / SPB, kb_hi = s_hi / SPB;
+    const int* tab = A.tables + (long long)b * A.max_blocks;
+
+    auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
+
+    // Projection rows of band T(jb) as the A operand: lane row a holds the
+    // weights of distance (w_lo - jb) - 32 + a (zero outside [0, R)).
+    auto load_p = [&](bf16x8 (&pv)[DR / 16], int jb) {
+        const int d = C.w_lo - jb - 32 + n;
+        const bool in = (unsigned)d < (unsigned)A.R;
+        const uint16_t* src = proj + (size_t)(in ? d : 0) * DR + 8 * hh;
+#pragma unroll
+        for (int st = 0; st < DR / 16; ++st) {
+            if (in) {
+                pv[st] = *reinterpret_cast<const bf16x8*>(src + 16 * st);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[st][i] = (__bf16)0.f;
+            }
+        }
+    };
+
+    // The start issues every independent load at once (q, r, the first two
+    // bands' projection rows, the block-table slice) behind a single wait,
+    // then the first copy, then the first two bands; so one HBM round trip
+    // precedes the copy instead of a chain of them.
+    bf16x8 rreg[DR / 16];  // r of the lane's column: the band's B operand
+    bf16x8 pv[DR / 16];    // projection rows of the next band
+    bf16x8 pv0[DR / 16];   // (start only) rows of the band before the first
+    const bool band_first = rel_active(js_lo);
+    if (band_first) {
+        load_p(pv0, js_lo - 32);
+        load_p(pv, js_lo);
+    }
+    load_q(C, A.q + trow * DQK, real, lane);
+#pragma unroll
+    for (int st = 0; st < DR / 16; ++st) {
+        if (real) {
+            rreg[st] = *reinterpret_cast<const bf16x8*>(A.r + trow * DR + 16 * st + 8 * hh);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rreg[st][i] = (__bf16)0.f;
+        }
+    }
+    init_acc(C);
+    bool bad = false;
+
+    int tab_base = kb_lo;
+    int tabv = (kb_lo + lane <= kb_hi) ? tab[kb_lo + lane] : -1;
+    // first key row (in the K/V caches) of stage s
+    auto stage_row = [&](int s, bool& okk) -> size_t {
+        const int kb = s / SPB;
+        if (kb - tab_base >= 64) {
+            tab_base += 64;
+            tabv = (tab_base + lane <= kb_hi) ? tab[tab_base + lane] : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        okk = phys >= 0 && phys < A.num_blocks;
+        return okk ? ((size_t)phys * A.Hkv + g) * BS + (size_t)(s % SPB) * HB : 0;
+    };
+
+    int koff[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) koff[st] = n * DQK + 8 * ((2 * st + hh) ^ (n & 15));
+    int vbo[DV / 32];
+    {
+        const int gq = lane >> 4, j = lane & 15, vr = 8 * (gq >> 1) + (j >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+            vbo[dt] = vr * DV + 32 * ((dt + vrot<DV>(vr)) & (DV / 32 - 1)) + 16 * (gq & 1) + 4 * (j & 3);
+    }
+
+    // T(jb) from the rows p into the ring: lane (n, hh) holds rows 8 i + 4 hh + 0..3
+    auto band = [&](const bf16x8 (&p)[DR / 16], int jb) {
+        f32x16 Tb = zero16();
+#pragma unroll
+        for (int st = 0; st < DR / 16; ++st) Tb = mfma32(p[st], rreg[st], Tb);
+        const int par = (jb >> 5) & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 v = {Tb[4 * i], Tb[4 * i + 1], Tb[4 * i + 2], Tb[4 * i + 3]};
+            *reinterpret_cast<f32x4*>(ring + 32 * par + 8 * i + 4 * hh) = v;
+        }
+        if (par == 0) {
+            const f32x4 v = {Tb[0], Tb[1], Tb[2], Tb[3]};
+            *reinterpret_cast<f32x4*>(ring + 64 + 4 * hh) = v;
+        }
+    };
+    // bias of subtile js in the score layout (register 8 c + e: key
+    // js + 16 c + 8 hh + e)
+    auto read_bias = [&](int js, RelVals& rb) {
+        const int par = (js >> 5) & 1;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int x = n - 16 * c - 8 * hh + 32 + 32 * par;
+            const float* p = ring + ((x - 7) & 63);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rb.v[8 * c + e] = p[7 - e];
+        }
+    };
+    auto compute = [&](const __bf16* Kc, const __bf16* Vc, int sub, int js, bool biased) {
+        const f32x16 sc = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
+        RelVals rb;
+        if (biased) read_bias(js, rb);
+        float x[16];
+        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, A.c1, lane, x);
+        if (__any(!C.m_set || sm_trigger(C, M))) {
+            if (__any(!C.m_set)) sm_init_ref(C, M, x);
+            if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+        }
+        bf16x8 pb[2];
+        sm_probs(C, x, pb);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int dt = 0; dt < DV / 32; ++dt)
+                C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * c) * DV, vbo[dt], DV), pb[c], C.O[dt]);
+        }
+    };
+
+    bool ok = false;
+    {
+        const size_t row = stage_row(s_lo, ok);
+        if (ok) kv_dma<DV, NW, HB>(K0, V0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
+    }
+    int band_js = INT_MIN;  // last band in the ring
+    int pv_js = INT_MIN;    // band whose projection rows pv holds
+    if (band_first) {
+        band(pv0, js_lo - 32);
+        band(pv, js_lo);
+        band_js = js_lo;
+    }
+
+    // One stage (two subtiles). Each band's projection rows are requested one
+    // subtile ahead; the next stage's first band's at the end of the stage,
+    // so they have landed by its barrier.
+    auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn, int s) {
+        vm_wait_all();
+        lds_barrier();
+        const bool ok_cur = ok;
+        bad = bad || !ok_cur;
+        const int js0 = s * HB, js1 = js0 + 32;
+        const bool comp0 = wave_active && ok_cur && !masked_all(C, js0, A.W);
+        const bool comp1 = wave_active && ok_cur && !masked_all(C, js1, A.W);
+        const bool bias0 = comp0 && bias_on(C, js0, A.R);
+        const bool bias1 = comp1 && bias_on(C, js1, A.R);
+        if (bias0 && band_js != js0) {
+            if (band_js != js0 - 32) {  // the ring lacks the previous band
+                load_p(pv, js0 - 32);
+                band(pv, js0 - 32);
+                pv_js = INT_MIN;
+            }
+            if (pv_js != js0) load_p(pv, js0);
+            band(pv, js0);
+            band_js = js0;
+        }
+        if (s < s_hi) {
+            const size_t row = stage_row(s + 1, ok);
+            if (ok) kv_dma<DV, NW, HB>(Kn, Vn, A.k + row * DQK, A.v + row * DV, L - (s + 1) * HB, wid, lane);
+        }
+        if (bias1 && band_js == js0) {
+            load_p(pv, js1);
+            pv_js = js1;
+        }
+        if (comp0) compute(Kc, Vc, 0, js0, bias0);
+        if (bias1) {
+            if (band_js != js0) {  // sub 0 had no band: build the ring first
+                load_p(pv, js0);
+                band(pv, js0);
+                pv_js = INT_MIN;
+            }
+            if (pv_js != js1) load_p(pv, js1);
+            band(pv, js1);
+            band_js = js1;
+        }
+        const int jn = js0 + HB;  // the next stage's first subtile
+        if (s < s_hi && rel_active(jn)) {
+            load_p(pv, jn);
+            pv_js = jn;
+        }
+        if (comp1) compute(Kc, Vc, 1, js1, bias1);
+    };
+    for (int s = s_lo;;) {
+        step(K0, V0, K1, V1, s);
+        if (++s > s_hi) break;
+        step(K1, V1, K0, V0, s);
+        if (++s > s_hi) break;
     }
 
     if (!wave_active || !real) return;
@@ -1428,6 +1701,20 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     } else {
         if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, false>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((prefill_kernel<64, false>), g, blk, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
+    const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
+    if (grid <= 0) return hipSuccess;
+    const dim3 g((unsigned)grid), blk(512);
+    if (a.W > 0) {
+        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_kernel<64, true>), g, blk, 0, s, a);
+    } else {
+        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128, false>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_kernel<64, false>), g, blk, 0, s, a);
     }
     return hipGetLastError();
 }

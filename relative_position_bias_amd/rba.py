@@ -76,6 +76,9 @@ _SIGNATURES = {
     "rba_decode_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
                                       ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _ptr,
                                       _size, _ptr, _ptr, _ptr]),
+    "rba_prefill_relproj": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _i32,
+                                           _i32, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr,
+                                           _ptr, _ptr]),
     "rba_decode_split_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
                                             ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
                                             _ptr, _size, _ptr]),
@@ -187,6 +190,43 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
         _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
         int(max_seq_len), _dev(out, torch.float32, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+    return out, lse
+
+
+def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, *, window: int, scale: float,
+                    max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                    sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rba_prefill_relproj: as prefill, with the bias made in the kernel from
+    r [total_q, Hq, 64] bf16 and proj [1 or Hq, R, 64] bf16 (rel_logits_proj
+    in linear-weight layout; R = proj.shape[1])."""
+    total_q, Hq, dqk = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    if r.dim() != 3 or r.shape[:2] != (total_q, Hq):
+        raise ValueError("r must be [total_q, Hq, d_r]")
+    d_r = r.shape[2]
+    if proj.dim() != 3 or proj.shape[2] != d_r:
+        raise ValueError("proj must be [proj_heads, R, d_r]")
+    proj_heads, R = proj.shape[0], proj.shape[1]
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be 2-D")
+    batch = cu_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, Hq, dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
+    _check(lib().rba_prefill_relproj(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(r, torch.bfloat16, "r"),
+        _dev(proj, torch.bfloat16, "proj"), d_r, proj_heads,
+        _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
+        int(max_seq_len), _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
+        _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+        _stream(stream)))
     return out, lse
 
 
