@@ -90,7 +90,12 @@ def algorithmic(b, kind):
     rows = b.rows
     q_bytes = rows * b.Hq * DQK * 2
     kv_bytes = keys * b.Hkv * (DQK + b.dv) * (1 if getattr(b, "kv_fp8", False) else 2)  # e4m3: 1 byte
-    rel_bytes = biased * b.Hq * 4
+    if getattr(b, "r", None) is not None:  # bias made in the kernel: r and the projection are read,
+        d_r = b.r.shape[2]                 # and each used bias entry costs a d_r-long dot product
+        rel_bytes = rows * b.Hq * d_r * 2 + b.proj.numel() * 2
+        flops += biased * b.Hq * 2 * d_r
+    else:
+        rel_bytes = biased * b.Hq * 4
     out_bytes = rows * b.Hq * b.dv * 4
     blocks = sum((L + 127) // 128 for L in seq_lens)
     table_bytes = blocks * 4
