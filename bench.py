@@ -322,7 +322,7 @@ def main():
     if t_split >= t_pre:
         achieved = b_split / t_split / 1e9
         # G * n_q <= 16 runs the 16-column split kernel
-        kname = "decode16_split_kernel<128>" if dec.Hq // dec.Hkv * dec.n_q <= 16 else "decode_split_kernel<128>"
+        kname = "decode16_split_kernel<128, false>" if dec.Hq // dec.Hkv * dec.n_q <= 16 else "decode_split_kernel<128, false>"
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
                     "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b_split,
