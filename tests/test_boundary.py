@@ -211,3 +211,26 @@ def test_fp8_decode_rejects_bad_scales():
         rc = lib.rba_decode_split_fp8(ctypes.byref(p), P, P, P, 2560, ks, vs, P, P, P, 1024, 16, 1, 131072, 8,
                                       P, 1 << 30, None)
         assert rc == rba.RBA_ERR_SHAPE, (ks, vs, rc)
+
+
+def test_relproj_prefill_rejects_bad_arguments():
+    """rba_prefill_relproj's own checks run before any HIP call (no device needed)."""
+    lib = rba.lib()
+    p = prm()
+
+    def call(r=P, proj=P, d_r=64, heads=1, q=P, out=P, batch=1):
+        return lib.rba_prefill_relproj(ctypes.byref(p), q, P, P, 64, r, proj, d_r, heads, P, P, P, 64, batch,
+                                       8192, 8192, None, None, out, None, None)
+
+    assert call(d_r=32) == rba.RBA_ERR_UNSUPPORTED
+    assert "d_r" in rba.last_error()
+    assert call(d_r=128) == rba.RBA_ERR_UNSUPPORTED
+    assert call(heads=3) == rba.RBA_ERR_SHAPE
+    assert call(heads=0) == rba.RBA_ERR_SHAPE
+    assert call(proj=None) == rba.RBA_ERR_NULL
+    assert call(proj=P + 8) == rba.RBA_ERR_UNSUPPORTED   # not 16-byte aligned
+    assert call(r=None) == rba.RBA_ERR_NULL
+    assert "r" in rba.last_error()
+    assert call(r=P + 4) == rba.RBA_ERR_UNSUPPORTED
+    assert call(q=None) == rba.RBA_ERR_NULL
+    assert call(batch=0) == rba.RBA_OK                    # empty call: nothing to do, no launch
