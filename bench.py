@@ -41,17 +41,32 @@ DQK = 128
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode16_split_kernel_paged_decode_16_disjoint_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_kernels.hip")
-HOST_SRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc", "rba_host.cpp")
+CSRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc")
+KERNEL_SRCS = [os.path.join(CSRC, "rba_kernels.hip"), os.path.join(CSRC, "rba_internal.h")]
+HOST_SRCS = [os.path.join(CSRC, "rba_host.cpp")]
+
+
+def code_digest(paths):
+    """SHA-256 of source files with comments, blank lines and trailing blanks
+    removed: it changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update(("\n".join(lines) + "\n").encode())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the decode split kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel code
     or the host code (which sets the launch, e.g. the split count) has changed
     since those counters were taken."""
-    import hashlib
-
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -59,9 +74,8 @@ def measured_traffic():
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    host = hashlib.sha256(open(HOST_SRC, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src or kv.get("host_source_sha256") != host:
+    if kv.get("kernel_code_sha256") != code_digest(KERNEL_SRCS) or \
+            kv.get("host_code_sha256") != code_digest(HOST_SRCS):
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 

@@ -43,6 +43,13 @@
 //     (one barrier per block); the next subtile's bias comes straight into
 //     registers. The block-table slice sits in a register (one entry per
 //     lane) so no load waits on a table read.
+//   * Prefill with the bias made in the kernel (rel = r @ rel_logits_proj,
+//     "Attention with a relative bias"): each wave forms the 63-distance band
+//     of a subtile from r (an MFMA operand held for the whole sweep) and the
+//     projection rows (from L2) with four more MFMAs, keeps the last two
+//     32-distance bands in a per-column LDS ring, and reads each lane's
+//     values back along the shear. The ring leaves room for half-block K/V
+//     stages only.
 //   * Decode: each of the 4 waves of a workgroup streams its own 32-key
 //     subtile of every block of the split without any barrier: K goes straight
 //     from HBM into MFMA operand registers, V into a wave-private LDS tile.
