@@ -726,7 +726,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
 constexpr int DR = 64;       // width of r
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
-template <int DV, bool WIN>
+template <int DV>
 __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
     constexpr int NW = 8;   // every wave issues copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
@@ -1716,13 +1716,8 @@ hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
-    if (a.W > 0) {
-        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_relproj_kernel<64, true>), g, blk, 0, s, a);
-    } else {
-        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128, false>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_relproj_kernel<64, false>), g, blk, 0, s, a);
-    }
+    if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prefill_relproj_kernel<64>), g, blk, 0, s, a);
     return hipGetLastError();
 }
 
