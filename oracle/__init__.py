@@ -68,7 +68,7 @@ def _f64(a):
 
 
 def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
-           rows=None, out=None, lse=None, sink=None, gate=None):
+           rows=None, out=None, lse=None, sink=None, gate=None, logit_scale=None):
     """Relative-bias GQA attention, float64, over contiguous K/V.
 
     q    [total_q, Hq, dqk]      rows of all sequences packed in order
@@ -81,10 +81,21 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
     sink, gate  optional [total_q, Hq] logits of the gated-attention output
                 (a sink in the softmax normaliser with zero value; a sigmoid
                 factor on the output); see oracle.c
+    logit_scale  optional [total_q]: the log-position scale of global layers
+                ("Inkling-Small on Gaudi 2", "What was built": a scale on q
+                and on the rel logits; the pages give no formula, so the
+                caller supplies one value per query row). Applied as written:
+                row t's q and rel are multiplied by logit_scale[t].
     Returns (out [total_q, Hq, dv], lse [total_q, Hq]) as float64.
     """
     lib = _load()
     q, k, v, rel = _f64(q), _f64(k), _f64(v), _f64(rel)
+    if logit_scale is not None:
+        f = _f64(logit_scale).reshape(-1)
+        if f.shape[0] != q.shape[0]:
+            raise ValueError("logit_scale must be [total_q]")
+        q = q * f[:, None, None]
+        rel = rel * f[:, None, None]
     q_lens = np.ascontiguousarray(q_lens, dtype=np.int64)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
     total_q, Hq, dqk = q.shape

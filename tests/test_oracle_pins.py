@@ -671,3 +671,87 @@ def test_relproj_mutants_are_caught(kind, monkeypatch):
     with pytest.raises(AssertionError):
         for d_r, R in [(8, 8)]:
             test_relproj_one_hot_selects_the_weight(d_r, R, shared=False)
+
+
+# ----------------------------------------------------------------------------
+# Log-position scale ("Inkling-Small on Gaudi 2", "What was built": a scale on
+# q and on the rel logits; no formula on the pages). Reading: the caller gives
+# one factor f_t per query row, which multiplies row t's q and rel.
+# ----------------------------------------------------------------------------
+
+def _logpos_ramp_case(f):
+    """q = 0 and rel = -a d: row t's weights over its keys are exp(-f_t a d)."""
+    L, Hq, R, dv, a = 9, 2, 16, 3, 0.7
+    rng = np.random.default_rng(5)
+    q = np.zeros((L, Hq, 4))
+    k = rng.standard_normal((L, 1, 4))
+    v = rng.standard_normal((L, 1, dv))
+    d = np.arange(R)
+    rel = np.broadcast_to(-a * d, (L, Hq, R)).copy()
+    out, _ = oracle.attend(q, k, v, rel, [L], [L], rel_extent=R, window=0, scale=0.3, logit_scale=f)
+    for t in range(L):
+        w = np.exp(-f[t] * a * (t - np.arange(t + 1)))
+        want = (w[:, None] * v[:t + 1, 0, :]).sum(0) / w.sum()
+        for h in range(Hq):
+            np.testing.assert_allclose(out[t, h], want, rtol=1e-12, atol=1e-12)
+
+
+def _logpos_q_case(f):
+    """rel = 0, q_t = e_0 and k_j = kappa_j e_0: weights exp(f_t scale kappa_j)."""
+    L, scale, dv = 7, 0.5, 2
+    q = np.zeros((L, 1, 4))
+    q[:, 0, 0] = 1.0
+    kappa = np.linspace(-2.0, 3.0, L)
+    k = np.zeros((L, 1, 4))
+    k[:, 0, 0] = kappa
+    v = np.arange(L * dv, dtype=np.float64).reshape(L, 1, dv)
+    rel = np.zeros((L, 1, 8))
+    out, lse = oracle.attend(q, k, v, rel, [L], [L], rel_extent=8, window=0, scale=scale, logit_scale=f)
+    for t in range(L):
+        z = f[t] * scale * kappa[:t + 1]
+        w = np.exp(z - z.max())
+        np.testing.assert_allclose(out[t, 0], (w[:, None] * v[:t + 1, 0, :]).sum(0) / w.sum(), rtol=1e-12)
+        np.testing.assert_allclose(lse[t, 0], z.max() + np.log(w.sum()), rtol=1e-12)
+
+
+LOGPOS_F = np.array([1.0, 1.3, 0.6, 2.0, 1.05, 0.9, 1.7, 1.2, 3.0])
+
+
+def test_logpos_scales_the_bias():
+    _logpos_ramp_case(LOGPOS_F)
+
+
+def test_logpos_scales_q_dot_k():
+    _logpos_q_case(LOGPOS_F[:7])
+
+
+def test_logpos_one_is_the_plain_oracle():
+    b = dict(q_lens=[40], seq_lens=[90])
+    rng = np.random.default_rng(9)
+    q, k, v = rng.standard_normal((40, 4, 8)), rng.standard_normal((90, 2, 8)), rng.standard_normal((90, 2, 5))
+    rel = rng.standard_normal((40, 4, 32))
+    o1, l1 = oracle.attend(q, k, v, rel, b["q_lens"], b["seq_lens"], rel_extent=32, window=20, scale=0.4)
+    o2, l2 = oracle.attend(q, k, v, rel, b["q_lens"], b["seq_lens"], rel_extent=32, window=20, scale=0.4,
+                           logit_scale=np.ones(40))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("kind", ["q_only", "rel_only", "squared"])
+def test_logpos_mutants_are_caught(kind, monkeypatch):
+    real = oracle.attend
+
+    def mutant(q, k, v, rel, q_lens, seq_lens, *, logit_scale=None, **kw):
+        if logit_scale is None:
+            return real(q, k, v, rel, q_lens, seq_lens, **kw)
+        f = np.asarray(logit_scale, dtype=np.float64).reshape(-1)
+        q, rel = np.asarray(q, dtype=np.float64), np.asarray(rel, dtype=np.float64)
+        if kind in ("q_only", "squared"):
+            q = q * (f * f if kind == "squared" else f)[:, None, None]
+        if kind in ("rel_only", "squared"):
+            rel = rel * (f * f if kind == "squared" else f)[:, None, None]
+        return real(q, k, v, rel, q_lens, seq_lens, **kw)
+
+    monkeypatch.setattr(oracle, "attend", mutant)
+    with pytest.raises(AssertionError):
+        test_logpos_scales_the_bias()
+        test_logpos_scales_q_dot_k()
