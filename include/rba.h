@@ -160,6 +160,37 @@ int rba_prefill_relproj(const rba_attn_params* params,
                         const float* sink, const float* gate,
                         float* out, float* lse, void* stream);
 
+/*
+ * Prefill and decode with a per-row logit scale: every logit of query row t,
+ * scale * q.k + bias, is multiplied by logit_scale[t]. Source: "Inkling-Small
+ * on Gaudi 2", section "What was built" (global layers apply a log-position
+ * scale to q and to the rel logits beyond 128K positions). The pages give no
+ * formula for the scale, so the caller computes one value per query row (for
+ * example from its absolute position); applying it to q and to the bias is
+ * the same as multiplying the row's logits by it.
+ *
+ *   logit_scale  device fp32, [total_q] for rba_prefill_logpos (row t of q)
+ *                and [batch * n_q] for rba_decode_logpos; finite values
+ *   all other arguments as rba_prefill / rba_decode (bf16 K/V; no sink or
+ *   gate). Errors: as rba_prefill / rba_decode; RBA_ERR_NULL if logit_scale
+ *   is NULL for a non-empty call, RBA_ERR_UNSUPPORTED if it is not 4-byte
+ *   aligned.
+ */
+int rba_prefill_logpos(const rba_attn_params* params,
+                       const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                       const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                       const float* logit_scale, float* out, float* lse, void* stream);
+
+int rba_decode_logpos(const rba_attn_params* params,
+                      const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                      const float* rel, const int32_t* seq_lens,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, const float* logit_scale,
+                      float* out, float* lse, void* stream);
+
 /* Host-only argument check of rba_prefill (no HIP call; same return codes). */
 int rba_validate_prefill(const rba_attn_params* params,
                          const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,

@@ -257,6 +257,7 @@ rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void*
     a.c1 = (float)((double)p->scale * 1.4426950408889634);
     a.v_scale = 1.0f;
     a.kv8 = 0;
+    a.lscale = nullptr;
     a.n_q = n_q;
     a.n_cg = (int32_t)ceil_div((int64_t)G * n_q, 32);
     a.splits = splits;
@@ -285,11 +286,11 @@ int rba_validate_prefill(const rba_attn_params* params, const void* q, const voi
                             max_blocks_per_seq, batch, max_q_len, max_seq_len, out, nullptr, &nothing);
 }
 
-int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
-                      int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
-                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
-                      int32_t max_seq_len, const float* sink, const float* gate, float* out, float* lse,
-                      void* stream) {
+static int prefill_impl(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                        int32_t max_seq_len, const float* sink, const float* gate, const float* lscale, float* out,
+                        float* lse, void* stream) {
     if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
     bool nothing;
     int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
@@ -304,6 +305,7 @@ int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* 
     a.r = nullptr;
     a.proj = nullptr;
     a.proj_heads = 0;
+    a.lscale = lscale;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;
     a.tables = block_tables;
@@ -327,6 +329,26 @@ int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* 
     hipError_t e = rba::launch_prefill(a, params->head_dim_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
+}
+
+int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                      int32_t max_seq_len, const float* sink, const float* gate, float* out, float* lse,
+                      void* stream) {
+    return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, sink, gate, nullptr, out, lse, stream);
+}
+
+int rba_prefill_logpos(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                       int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                       int32_t max_seq_len, const float* logit_scale, float* out, float* lse, void* stream) {
+    if (batch > 0 && max_q_len > 0 && logit_scale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
+    if (!aligned4(logit_scale)) return fail(RBA_ERR_UNSUPPORTED, "logit_scale must be 4-byte aligned");
+    return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, nullptr, nullptr, logit_scale, out, lse,
+                        stream);
 }
 
 int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -361,6 +383,7 @@ int rba_prefill_relproj(const rba_attn_params* params, const void* q, const void
     a.r = static_cast<const uint16_t*>(r);
     a.proj = static_cast<const uint16_t*>(rel_proj);
     a.proj_heads = proj_heads;
+    a.lscale = nullptr;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;
     a.tables = block_tables;
@@ -514,6 +537,28 @@ int rba_decode_gated(const rba_attn_params* params, const void* q, const void* k
     if (e != hipSuccess) return hip_fail(e, "decode split launch");
     return rba_decode_combine_gated(params, batch, n_q, splits, workspace, workspace_bytes, sink, gate, out, lse,
                                     stream);
+}
+
+int rba_decode_logpos(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                      int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes, const float* logit_scale,
+                      float* out, float* lse, void* stream) {
+    bool nothing;
+    int32_t splits = 0;
+    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                             workspace_bytes, out, lse, true, &splits, &nothing);
+    if (rc || nothing) return rc;
+    if (logit_scale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
+    if (!aligned4(logit_scale)) return fail(RBA_ERR_UNSUPPORTED, "logit_scale must be 4-byte aligned");
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    a.lscale = logit_scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
 }
 
 static int check_kv_scales(float k_scale, float v_scale) {

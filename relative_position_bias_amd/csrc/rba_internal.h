@@ -24,6 +24,7 @@ struct PrefillArgs {
     const uint16_t* r;        // bf16 [total_q, Hq, 64] R-branch vectors (bias made in the kernel), or null
     const uint16_t* proj;     // bf16 [proj_heads, R, 64] rel_logits_proj (linear-weight layout)
     int32_t proj_heads;       // 1 (shared) or Hq
+    const float* lscale;      // fp32 [total_q] per-row logit scale, or null (1)
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
     float c1;                 // scale * log2(e)
@@ -47,6 +48,7 @@ struct DecodeArgs {
     int32_t Hq, Hkv, G, R, W;
     float c1;                 // scale * log2(e), times the K dequantization scale for e4m3 K/V
     float v_scale;            // V dequantization scale (1 for bf16 K/V)
+    const float* lscale;      // fp32 [batch * n_q] per-row logit scale, or null (1)
     int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3 (OCP FP8, one byte)
     int32_t n_q, n_cg, splits, bps;   // column groups of 32 (head, token) pairs; blocks per split
 };

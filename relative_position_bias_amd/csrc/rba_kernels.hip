@@ -228,12 +228,13 @@ __device__ __forceinline__ f32x16 qk_regs(const bf16x8 (&kreg)[8], const bf16x8 
 // lane & 31); if `has_bias`, `rb` is the lane's staged bias row.
 template <int DV>
 __device__ __forceinline__ float sm_scores(const Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
-                                           bool need_mask, int js, int W, float c1, int lane, float (&x)[16]) {
+                                           bool need_mask, int js, int W, float c1, float l2e, int lane,
+                                           float (&x)[16]) {
     const int hh = lane >> 5;
     if (has_bias) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            x[r] = fmaf(s[r], c1, fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], LOG2E, -C.m_ref));
+            x[r] = fmaf(s[r], c1, fmaf(rb[16 * (1 - (r >> 3)) + 7 - (r & 7)], l2e, -C.m_ref));
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], c1, -C.m_ref);
@@ -307,9 +308,9 @@ __device__ __forceinline__ bool need_mask_of(const Cols<DV>& C, int js, int W) {
 // A operand: V^T rows 32 dt + (lane & 31), keys 16 c + 8 (lane>>5) .. +8.
 template <int DV, class VRead>
 __device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool has_bias, const float* rb,
-                                           int js, int W, float c1, int lane, VRead vread) {
+                                           int js, int W, float c1, float l2e, int lane, VRead vread) {
     float x[16];
-    float M = sm_scores(C, s, has_bias, rb, need_mask_of(C, js, W), js, W, c1, lane, x);
+    float M = sm_scores(C, s, has_bias, rb, need_mask_of(C, js, W), js, W, c1, l2e, lane, x);
     if (__any(!C.m_set || sm_trigger(C, M))) {
         if (__any(!C.m_set)) sm_init_ref(C, M, x);
         if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
@@ -516,12 +517,12 @@ __device__ __forceinline__ float rel_bias(const RelVals& rv, int r, int pos, int
 // sm_scores with the bias taken from registers.
 template <int DV>
 __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s, bool has_bias, const RelVals& rv,
-                                              bool inside, bool need_mask, int js, int W, int R, float c1, int lane,
-                                              float (&x)[16]) {
+                                              bool inside, bool need_mask, int js, int W, int R, float c1, float l2e,
+                                              int lane, float (&x)[16]) {
     if (has_bias) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            x[r] = fmaf(s[r], c1, fmaf(rel_bias(rv, r, C.pos, js, R, inside, lane), LOG2E, -C.m_ref));
+            x[r] = fmaf(s[r], c1, fmaf(rel_bias(rv, r, C.pos, js, R, inside, lane), l2e, -C.m_ref));
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = fmaf(s[r], c1, -C.m_ref);
@@ -541,8 +542,10 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
     return halves_max(M);
 }
 
-template <int DV, bool WIN>
-__global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
+// LS: each query row's logits are multiplied by A.lscale[row] (the
+// log-position scale of global layers, "What was built"); otherwise by 1.
+template <int DV, bool WIN, bool LS>
+__device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     constexpr int NW = WIN ? 8 : 4;  // waves that issue the K/V copies
     __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 K1[BS * DQK];
@@ -574,6 +577,8 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     const int r = qa + n;
     const bool real = r < q_len;
     const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
+    const float fls = (LS && real) ? A.lscale[q_start + r] : 1.f;  // the row's logit scale
+    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
 
     Cols<DV> C;
     C.pos = real ? ctx + r : -1;
@@ -655,7 +660,7 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
             auto scores = [&](float(&x)[16]) {
                 const f32x16 s = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
                 return sm_scores_rv(C, s, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W), js,
-                                    A.W, A.R, A.c1, lane, x);
+                                    A.W, A.R, c1f, l2f, lane, x);
             };
             auto finish = [&](float M, float(&x)[16]) {
                 if (__any(!C.m_set || sm_trigger(C, M))) {
@@ -698,6 +703,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
     if (!wave_active || !real) return;
     store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
               A.gate ? A.gate[trow] : INFINITY, lane);
+}
+
+template <int DV, bool WIN>
+__global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
+    prefill_body<DV, WIN, false>(A);
+}
+
+template <int DV, bool WIN>
+__global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A) {
+    prefill_body<DV, WIN, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -882,7 +897,7 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
         RelVals rb;
         if (biased) read_bias(js, rb);
         float x[16];
-        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, A.c1, lane, x);
+        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, A.c1, LOG2E, lane, x);
         if (__any(!C.m_set || sm_trigger(C, M))) {
             if (__any(!C.m_set)) sm_init_ref(C, M, x);
             if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
@@ -1131,8 +1146,8 @@ struct Kv<true> {
     }
 };
 
-template <int DV, bool KV8>
-__global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
+template <int DV, bool KV8, bool LS>
+__device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     using KV = Kv<KV8>;
     const char* const kbase = reinterpret_cast<const char*>(A.k);
     const char* const vbase = reinterpret_cast<const char*>(A.v);
@@ -1155,6 +1170,8 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
     const int hl = real ? c % A.G : 0;
     const int h = g * A.G + hl;
     const long long trow = (long long)(b * A.n_q + tt) * A.Hq + h;
+    const float fls = (LS && real) ? A.lscale[b * A.n_q + tt] : 1.f;  // the row's logit scale
+    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
 
     Cols<DV> C;
     C.pos = real ? L - A.n_q + tt : -1;
@@ -1235,7 +1252,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             if (ok_next) KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, wid, lane);
             if (brel) rel_store(Rw, rr, lane);
             __builtin_amdgcn_wave_barrier();
-            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
+            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, c1f, l2f, lane,
                            [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
             __builtin_amdgcn_wave_barrier();
             ok_cur = ok_next;
@@ -1263,7 +1280,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             const f32x16 s = qk_regs(kb16, C.qreg);
             if (brel) rel_store(Rw, rr, lane);
             __builtin_amdgcn_wave_barrier();
-            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, A.c1, lane,
+            softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, c1f, l2f, lane,
                            [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
             __builtin_amdgcn_wave_barrier();
         }
@@ -1318,6 +1335,16 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A
             A.part_lse[prow] = any_bad ? NAN : (M > -INFINITY ? (M + __log2f(den)) * LN2 : -INFINITY);
         }
     }
+}
+
+template <int DV, bool KV8>
+__global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
+    decode_split_body<DV, KV8, false>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(256, 2) decode_split_logpos_kernel(const DecodeArgs A) {
+    decode_split_body<DV, false, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1405,8 +1432,8 @@ struct Decode16Lds {
     static constexpr int TOTAL = (4 * V_BYTES > MERGE) ? 4 * V_BYTES : MERGE;
 };
 
-template <int DV, bool KV8>
-__global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs A) {
+template <int DV, bool KV8, bool LS>
+__device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     using KV = Kv<KV8>;
     typedef typename std::conditional<KV8, uint8_t, uint16_t>::type KElem;
     const KElem* const kel = reinterpret_cast<const KElem*>(A.k);
@@ -1430,6 +1457,8 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
     const long long trow = (long long)(b * A.n_q + tt) * A.Hq + h;
     const int pos = real ? L - A.n_q + tt : -1;
     const float* relrow = A.rel + trow * A.R;
+    const float fls = (LS && real) ? A.lscale[b * A.n_q + tt] : 1.f;  // the row's logit scale
+    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
     // wave-uniform column range (positions of the first and last real column)
     const int w_lo = L - A.n_q, w_hi = L - A.n_q + (ncols - 1) / A.G;
     const bool phantom = ncols < 16;
@@ -1519,13 +1548,13 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
         const int d0 = pos - (js + 8 * q);  // distance of the lane's key i is d0 - i
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = S[i >> 2][i & 3] * A.c1 - m_ref;
+        for (int i = 0; i < 8; ++i) x[i] = S[i >> 2][i & 3] * c1f - m_ref;
         if (brel) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int d = d0 - i;
                 const float rv = relrow[min(max(d, 0), A.R - 1)];
-                x[i] += (d >= 0 && d < A.R && pos >= 0) ? rv * LOG2E : 0.f;
+                x[i] += (d >= 0 && d < A.R && pos >= 0) ? rv * l2f : 0.f;
             }
         }
         if (nmask) {
@@ -1612,6 +1641,16 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
             A.part_lse[prow] = any_bad ? NAN : (Mx > -INFINITY ? (Mx + __log2f(den)) * LN2 : -INFINITY);
         }
     }
+}
+
+template <int DV, bool KV8>
+__global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs A) {
+    decode16_split_body<DV, KV8, false>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(256, 2) decode16_split_logpos_kernel(const DecodeArgs A) {
+    decode16_split_body<DV, false, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1702,6 +1741,16 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
+    if (a.lscale != nullptr) {  // per-row logit scale
+        if (a.W > 0) {
+            if (dv == 128) hipLaunchKernelGGL((prefill_logpos_kernel<128, true>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((prefill_logpos_kernel<64, true>), g, blk, 0, s, a);
+        } else {
+            if (dv == 128) hipLaunchKernelGGL((prefill_logpos_kernel<128, false>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((prefill_logpos_kernel<64, false>), g, blk, 0, s, a);
+        }
+        return hipGetLastError();
+    }
     if (a.W > 0) {  // windowed: every subtile streams bias
         if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((prefill_kernel<64, true>), g, blk, 0, s, a);
@@ -1726,6 +1775,16 @@ hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(256);
     const bool kv8 = a.kv8 != 0;
+    if (a.lscale != nullptr) {  // per-row logit scale (bf16 K/V only)
+        if (a.G * a.n_q <= 16) {
+            if (dv == 128) hipLaunchKernelGGL((decode16_split_logpos_kernel<128>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((decode16_split_logpos_kernel<64>), g, blk, 0, s, a);
+        } else {
+            if (dv == 128) hipLaunchKernelGGL((decode_split_logpos_kernel<128>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((decode_split_logpos_kernel<64>), g, blk, 0, s, a);
+        }
+        return hipGetLastError();
+    }
     if (a.G * a.n_q <= 16) {  // one 16-column group (n_cg == 1)
         if (dv == 128) {
             if (kv8) hipLaunchKernelGGL((decode16_split_kernel<128, true>), g, blk, 0, s, a);

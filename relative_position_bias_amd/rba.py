@@ -76,6 +76,10 @@ _SIGNATURES = {
     "rba_decode_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
                                       ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _ptr,
                                       _size, _ptr, _ptr, _ptr]),
+    "rba_prefill_logpos": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                          _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr, _ptr]),
+    "rba_decode_logpos": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                         _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr, _ptr, _ptr, _ptr]),
     "rba_prefill_relproj": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _i32,
                                            _i32, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr,
                                            _ptr, _ptr]),
@@ -153,12 +157,14 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
             max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, want_lse: bool = False,
             sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+            logit_scale: Optional[torch.Tensor] = None,
             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill. q [total_q, Hq, 128] bf16; k_cache [nb, Hkv, 128, 128] bf16;
     v_cache [nb, Hkv, 128, dv] bf16; rel [total_q, Hq, R] fp32; cu_q [B+1],
     seq_lens [B], block_tables [B, max_blocks] int32. max_q_len / max_seq_len
     are host-side bounds (no device read happens here). With sink and/or gate
-    (fp32 [total_q, Hq]) rba_prefill_gated runs."""
+    (fp32 [total_q, Hq]) rba_prefill_gated runs; with logit_scale (fp32
+    [total_q]) rba_prefill_logpos."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -173,6 +179,19 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     if lse is None and want_lse:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
+    if logit_scale is not None:
+        if sink is not None or gate is not None:
+            raise ValueError("logit_scale cannot be combined with sink / gate")
+        if tuple(logit_scale.shape) != (total_q,):
+            raise ValueError("logit_scale must be [total_q]")
+        _check(lib().rba_prefill_logpos(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+            _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
+            int(max_seq_len), _dev(logit_scale, torch.float32, "logit_scale"), _dev(out, torch.float32, "out"),
+            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+        return out, lse
     if sink is not None or gate is not None:
         _check(lib().rba_prefill_gated(
             ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
@@ -272,12 +291,14 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            want_lse: bool = False, kv_scales: Optional[Tuple[float, float]] = None,
            sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+           logit_scale: Optional[torch.Tensor] = None,
            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_decode (split-KV + combine). q [batch*n_q, Hq, 128] bf16; rel
     [batch*n_q, Hq, R] fp32. `workspace` (uint8, on the GPU) is allocated with
     torch if not given. With kv_scales = (k_scale, v_scale) the caches are
     e4m3 bytes and rba_decode_fp8 runs. With sink and/or gate (fp32
-    [batch*n_q, Hq]) the merge is rba_decode_combine_gated."""
+    [batch*n_q, Hq]) the merge is rba_decode_combine_gated. With logit_scale
+    (fp32 [batch*n_q]; bf16 caches, no sink / gate) rba_decode_logpos runs."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
     L = lib()
@@ -288,6 +309,20 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    if logit_scale is not None:
+        if sink is not None or gate is not None or kv_scales is not None:
+            raise ValueError("logit_scale cannot be combined with sink / gate / kv_scales")
+        if tuple(logit_scale.shape) != (rows,):
+            raise ValueError("logit_scale must be [batch * n_q]")
+        _check(L.rba_decode_logpos(
+            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+            _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+            block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
+            _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _dev(logit_scale, torch.float32, "logit_scale"), _dev(out, torch.float32, "out"),
+            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+        return out, lse
     if sink is not None or gate is not None:
         splits = int(num_splits) or plan_splits(Hq, p.num_heads_kv, dv, p.rel_extent, window, scale, batch, n_q,
                                                 int(max_seq_len), _num_cus(q.device))

@@ -49,7 +49,8 @@ def oracle_batch(batch: workloads.Batch, rows=None):
         v = oracle.unpage(vb, [list(range(nb))], [L])
         def gated(a, b_):
             return dict(sink=batch.sink[a:b_].double().numpy() if batch.sink is not None else None,
-                        gate=batch.gate[a:b_].double().numpy() if batch.gate is not None else None)
+                        gate=batch.gate[a:b_].double().numpy() if batch.gate is not None else None,
+                        logit_scale=batch.lscale[a:b_].double().numpy() if batch.lscale is not None else None)
         if local is None:
             o, l = oracle.attend(batch.q[start:start + ql].double().numpy(), k, v,
                                  rel_rows(start, start + ql), [ql], [L], **kw,
@@ -73,6 +74,8 @@ def run_prefill(b: workloads.Batch, want_lse=False, **kw):
         kw.setdefault("sink", b.sink)
     if b.gate is not None:
         kw.setdefault("gate", b.gate)
+    if b.lscale is not None:
+        kw.setdefault("logit_scale", b.lscale)
     if b.r is not None:
         return rba.prefill_relproj(b.q, b.k_cache, b.v_cache, b.r, b.proj, b.cu_q, b.seq_lens, b.block_tables,
                                    window=b.W, scale=b.scale, max_q_len=b.max_q_len,
@@ -89,6 +92,8 @@ def run_decode(b: workloads.Batch, num_splits=0, want_lse=False, **kw):
         kw.setdefault("sink", b.sink)
     if b.gate is not None:
         kw.setdefault("gate", b.gate)
+    if b.lscale is not None:
+        kw.setdefault("logit_scale", b.lscale)
     return rba.decode(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
                       window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
                       want_lse=want_lse, **kw)

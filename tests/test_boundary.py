@@ -234,3 +234,22 @@ def test_relproj_prefill_rejects_bad_arguments():
     assert call(r=P + 4) == rba.RBA_ERR_UNSUPPORTED
     assert call(q=None) == rba.RBA_ERR_NULL
     assert call(batch=0) == rba.RBA_OK                    # empty call: nothing to do, no launch
+
+
+def test_logpos_rejects_missing_or_misaligned_scale():
+    """Checks of rba_prefill_logpos / rba_decode_logpos run before any HIP call."""
+    lib = rba.lib()
+    p = prm()
+    rc = lib.rba_prefill_logpos(ctypes.byref(p), P, P, P, 64, P, P, P, P, 64, 1, 8192, 8192, None, P, None, None)
+    assert rc == rba.RBA_ERR_NULL and "logit_scale" in rba.last_error()
+    rc = lib.rba_prefill_logpos(ctypes.byref(p), P, P, P, 64, P, P, P, P, 64, 1, 8192, 8192, P + 2, P, None, None)
+    assert rc == rba.RBA_ERR_UNSUPPORTED
+    assert lib.rba_prefill_logpos(ctypes.byref(p), P, P, P, 64, P, P, P, P, 64, 0, 8192, 8192, None, P, None,
+                                  None) == rba.RBA_OK   # empty call
+    d = dprm()
+    rc = lib.rba_decode_logpos(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, 8, P, 1 << 30, None,
+                               P, None, None)
+    assert rc == rba.RBA_ERR_NULL
+    rc = lib.rba_decode_logpos(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, 8, P, 1 << 30, P + 2,
+                               P, None, None)
+    assert rc == rba.RBA_ERR_UNSUPPORTED

@@ -65,6 +65,10 @@ WORKLOADS["inkling2_verify_b1_100k_gated"] = dict(kind="decode", batch=1, seq_le
 # head; the pages do not give the width) and one shared projection.
 WORKLOADS["local_prefill_8k_relproj"] = dict(WORKLOADS["local_prefill_8k"], d_r=64)
 WORKLOADS["global_chunked_prefill_32k_relproj"] = dict(WORKLOADS["global_chunked_prefill_32k"], d_r=64)
+# Global-layer calls with a per-row log-position logit scale.
+WORKLOADS["global_chunked_prefill_32k_logpos"] = dict(WORKLOADS["global_chunked_prefill_32k"], logpos=True)
+WORKLOADS["paged_decode_16x8k_128k_disjoint_logpos"] = dict(WORKLOADS["paged_decode_16x8k_128k_disjoint"],
+                                                          logpos=True)
 # The decode workloads again over e4m3 K/V caches.
 for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k", "verify_decode_b8_100k"):
     WORKLOADS[_name + "_fp8"] = dict(WORKLOADS[_name], kv_fp8=True)
@@ -98,6 +102,7 @@ class Batch:
     v_scale: float = 1.0
     r: Optional[torch.Tensor] = None      # bf16 [rows, Hq, d_r] R-branch vectors (rel not given)
     proj: Optional[torch.Tensor] = None   # bf16 [1 or Hq, R, d_r] rel_logits_proj, linear-weight layout
+    lscale: Optional[torch.Tensor] = None  # fp32 [rows] per-row logit scale (log-position scale)
 
     def to(self, device) -> "Batch":
         kw = {}
@@ -150,6 +155,13 @@ def _gated(rows: int, Hq: int, gen: torch.Generator) -> dict:
     return dict(sink=sink, gate=gate)
 
 
+def _logpos(rows: int, gen: torch.Generator) -> torch.Tensor:
+    """Synthetic per-row logit scales, uniform in [1, 1.25] (drawn last). The
+    pages give no formula for the log-position scale; a factor a little above
+    1 is what such a scale does to rows past its threshold."""
+    return 1.0 + 0.25 * torch.rand(rows, generator=gen, dtype=torch.float32)
+
+
 def _to_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
     """x / scale rounded to e4m3 by torch, as raw bytes (chunked)."""
     out = torch.empty(x.shape, dtype=torch.uint8)
@@ -169,7 +181,8 @@ def _tables_tensor(tables: List[List[int]], max_blocks: int) -> torch.Tensor:
 
 def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv: int, dv: int, R: int,
                  W: int, permute: bool = True, scale: Optional[float] = None,
-                 extra_blocks: int = 0, gated: bool = False, d_r: int = 0, proj_heads: int = 1) -> Batch:
+                 extra_blocks: int = 0, gated: bool = False, d_r: int = 0, proj_heads: int = 1,
+                 logpos: bool = False) -> Batch:
     """Sequences with ctx_lens[b] cached tokens followed by q_lens[b] new ones
     (whose K/V are already in the cache). One pool holds every sequence's
     blocks, disjoint, permuted if `permute`. With d_r > 0 the bias is given
@@ -199,6 +212,8 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
     _poison(k_cache, v_cache, tables, seq_lens)
     max_blocks = max(nblk)
     extra = _gated(total_q, Hq, gen) if gated else {}
+    if logpos:
+        extra["lscale"] = _logpos(total_q, gen)
     cu = [0]
     for ql in q_lens:
         cu.append(cu[-1] + ql)
@@ -214,7 +229,7 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
 def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: int, W: int,
                 seq_lens: Optional[List[int]] = None, len_range=None, seq_len: Optional[int] = None,
                 pool_blocks: Optional[int] = None, scale: Optional[float] = None, kv_fp8: bool = False,
-                gated: bool = False) -> Batch:
+                gated: bool = False, logpos: bool = False) -> Batch:
     """`batch` sequences decoding n_q tokens each. Lengths: explicit, one fixed
     `seq_len`, or uniform integers in `len_range` (inclusive). With
     pool_blocks=None every sequence gets its own blocks (one global
@@ -248,6 +263,8 @@ def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: 
             tables.append(torch.randperm(num_blocks, generator=gen)[:n].tolist())
     _poison(k_cache, v_cache, tables, seq_lens)
     kw = _gated(batch * n_q, Hq, gen) if gated else {}
+    if logpos:
+        kw["lscale"] = _logpos(batch * n_q, gen)
     if kv_fp8:
         k_cache = _to_e4m3(k_cache, K_SCALE_FP8)
         v_cache = _to_e4m3(v_cache, V_SCALE_FP8)
@@ -274,7 +291,8 @@ def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
                  max_q_len=b - a, max_seq_len=b,
                  sink=full.sink[a:b] if full.sink is not None else None,
                  gate=full.gate[a:b] if full.gate is not None else None,
-                 r=full.r[a:b] if full.r is not None else None, proj=full.proj)
+                 r=full.r[a:b] if full.r is not None else None, proj=full.proj,
+                 lscale=full.lscale[a:b] if full.lscale is not None else None)
 
 
 def build(name: str, seed: int = 0) -> Batch:
@@ -288,7 +306,7 @@ def build(name: str, seed: int = 0) -> Batch:
         total = w.pop("total")
         w.pop("chunk")
         return make_prefill(seed, [total], [0], w["Hq"], w["Hkv"], w["dv"], w["R"], w["W"],
-                            d_r=w.get("d_r", 0), proj_heads=w.get("proj_heads", 1))
+                            d_r=w.get("d_r", 0), proj_heads=w.get("proj_heads", 1), logpos=w.get("logpos", False))
     return make_decode(seed, **w)
 
 
