@@ -7,6 +7,11 @@ the passages of the pages it follows).
 
 ``attend`` takes float64 NumPy arrays with contiguous (un-paged) keys and
 values; un-paging a block-table cache is the caller's job (a plain gather).
+
+Two readings have no formula on the pages: the gated output (sink and gate)
+and the log-position logit scale. Their code follows the reading stated where
+it is implemented and is pinned to that reading; parity against the pages is
+unpinned for them.
 """
 from __future__ import annotations
 
