@@ -262,6 +262,7 @@ rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void*
     a.n_cg = (int32_t)ceil_div((int64_t)G * n_q, 32);
     a.splits = splits;
     a.bps = (int32_t)ceil_div(decode_nb_eff(p, n_q, max_seq_len), splits);
+    a.wide = (int64_t)batch * a.Hkv * a.n_cg * splits <= device_cus() ? 1 : 0;
     return a;
 }
 

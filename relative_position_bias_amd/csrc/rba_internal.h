@@ -51,6 +51,7 @@ struct DecodeArgs {
     const float* lscale;      // fp32 [batch * n_q] per-row logit scale, or null (1)
     int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3 (OCP FP8, one byte)
     int32_t n_q, n_cg, splits, bps;   // column groups of 32 (head, token) pairs; blocks per split
+    int32_t wide;             // 1: the grid fits one workgroup per CU (8-wave e4m3 dv-64 variant)
 };
 
 struct CombineArgs {

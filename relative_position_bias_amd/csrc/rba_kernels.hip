@@ -997,13 +997,13 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
 // no block waits on a dependent table load. The four waves' partial softmax
 // states are merged through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int DV>
+template <int DV, int NW = 4>
 struct DecodeLds {
     static constexpr int V_BYTES = 32 * vrow<DV>() * 2;
     static constexpr int R_BYTES = 32 * RROW * 4;
     static constexpr int WAVE = V_BYTES + R_BYTES;
-    static constexpr int MERGE = 4 * 32 * DV * 4 + 2 * 4 * 32 * 4;
-    static constexpr int TOTAL = (4 * WAVE > MERGE) ? 4 * WAVE : MERGE;
+    static constexpr int MERGE = NW * 32 * DV * 4 + 2 * NW * 32 * 4;
+    static constexpr int TOTAL = (NW * WAVE > MERGE) ? NW * WAVE : MERGE;
 };
 
 // K subtile (32 keys) of one block, in the MFMA A-operand layout: lane holds
@@ -1146,14 +1146,20 @@ struct Kv<true> {
     }
 };
 
-template <int DV, bool KV8, bool LS>
+// NW = 4: wave w takes the 32-key subtile w of every block of the split.
+// NW = 8 (one workgroup per CU): waves 4..7 take the odd blocks and waves
+// 0..3 the even ones, so a workgroup keeps two blocks of loads in flight.
+template <int DV, bool KV8, bool LS, int NW = 4>
 __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     using KV = Kv<KV8>;
+    using Lds = DecodeLds<DV, NW>;
     const char* const kbase = reinterpret_cast<const char*>(A.k);
     const char* const vbase = reinterpret_cast<const char*>(A.v);
-    __shared__ __attribute__((aligned(16))) char smem[DecodeLds<DV>::TOTAL];
+    __shared__ __attribute__((aligned(16))) char smem[Lds::TOTAL];
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
+    constexpr int STEP = NW / 4;                       // blocks between a wave's steps
+    const int sub = wid & 3, par = wid >> 2;            // subtile in the block; block parity
     int id = blockIdx.x;
     const int g = id % A.Hkv;
     id /= A.Hkv;
@@ -1187,15 +1193,16 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
     const int s_lo = kb_first + split * A.bps;
     const int s_hi = min(s_lo + A.bps, nb);
-    __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * DecodeLds<DV>::WAVE);
-    float* Rw = reinterpret_cast<float*>(smem + wid * DecodeLds<DV>::WAVE + DecodeLds<DV>::V_BYTES);
+    __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Lds::WAVE);
+    float* Rw = reinterpret_cast<float*>(smem + wid * Lds::WAVE + Lds::V_BYTES);
     const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
-    // This wave's subtiles that are not entirely masked form one run of blocks.
-    int ka = s_lo, kz = s_hi - 1;
-    while (ka <= kz && masked_all(C, ka * BS + 32 * wid, A.W)) ++ka;
-    while (kz >= ka && masked_all(C, kz * BS + 32 * wid, A.W)) --kz;
+    // This wave's subtiles that are not entirely masked form one run of
+    // blocks ka, ka + STEP, ..., kz.
+    int ka = s_lo + par, kz = ka <= s_hi - 1 ? ka + (s_hi - 1 - ka) / STEP * STEP : ka - STEP;
+    while (ka <= kz && masked_all(C, ka * BS + 32 * sub, A.W)) ka += STEP;
+    while (kz >= ka && masked_all(C, kz * BS + 32 * sub, A.W)) kz -= STEP;
 
     // split's block-table slice, lane i = entry tab_base + i
     int tab_base = ka;
@@ -1218,39 +1225,49 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
         };
         typename KV::KReg kr[8];
         typename KV::template VRegs<DV> vs;
+        // the bias of a subtile is loaded one block ahead too, so that the
+        // blocks near the queries do not wait a memory round trip each (the
+        // per-row scales of the log-position variant leave no registers for
+        // it: there it is loaded in the block's own step)
+        constexpr bool REL_AHEAD = !LS;
+        RelRegs rr;
         bool ok_cur = false;
         if (ka <= kz) {
             const size_t base = block_base(ka, ok_cur);
             if (ok_cur) {
-                KV::k_sub(kr, kbase + base * DQK * KV::ESZ, wid, lane);
-                KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, wid, L - ka * BS, lane);
+                KV::k_sub(kr, kbase + base * DQK * KV::ESZ, sub, lane);
+                KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, sub, L - ka * BS, lane);
             }
+            if (REL_AHEAD && bias_on(C, ka * BS + 32 * sub, A.R))
+                rel_load(rr, C.relrow, C.pos, ka * BS + 32 * sub, A.R, lane);
         }
 #pragma unroll 1
-        for (int kb = ka; kb <= kz; ++kb) {
-            const int js = kb * BS + 32 * wid;
+        for (int kb = ka; kb <= kz; kb += STEP) {
+            const int js = kb * BS + 32 * sub;
             bool ok_next = false;
-            const size_t base_next = kb < kz ? block_base(kb + 1, ok_next) : 0;
+            const size_t base_next = kb < kz ? block_base(kb + STEP, ok_next) : 0;
+            const bool brel = bias_on(C, js, A.R);
+            const bool brel_next = kb < kz && bias_on(C, js + STEP * BS, A.R);
             if (!ok_cur) {
                 bad = true;
                 if (ok_next) {
-                    KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, wid, lane);
-                    KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, wid, L - (kb + 1) * BS, lane);
+                    KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, sub, lane);
+                    KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, sub, L - (kb + STEP) * BS, lane);
                 }
+                if (REL_AHEAD && brel_next) rel_load(rr, C.relrow, C.pos, js + STEP * BS, A.R, lane);
                 ok_cur = ok_next;
                 continue;
             }
-            const bool brel = bias_on(C, js, A.R);
-            RelRegs rr;
-            if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
+            if (!REL_AHEAD && brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
             KV::template v_store<DV>(Vw, vs, lane);
-            if (ok_next) KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, wid, L - (kb + 1) * BS, lane);
+            if (ok_next) KV::template v_load<DV>(vs, vbase + base_next * DV * KV::ESZ, sub, L - (kb + STEP) * BS, lane);
             bf16x8 kb16[8];
 #pragma unroll
             for (int st = 0; st < 8; ++st) kb16[st] = KV::op(kr[st]);
             const f32x16 s = qk_regs(kb16, C.qreg);
-            if (ok_next) KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, wid, lane);
+            if (ok_next) KV::k_sub(kr, kbase + base_next * DQK * KV::ESZ, sub, lane);
             if (brel) rel_store(Rw, rr, lane);
+            if (REL_AHEAD && brel_next) rel_load(rr, C.relrow, C.pos, js + STEP * BS, A.R, lane);
             __builtin_amdgcn_wave_barrier();
             softmax_pv<DV>(C, s, brel, rel_row_ptr(Rw, C.pos, lane), js, A.W, c1f, l2f, lane,
                            [&](int dt, int cc) { return v_operand(Vw, vrow<DV>(), 16 * cc, 32 * dt, lane); });
@@ -1258,8 +1275,8 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
             ok_cur = ok_next;
         }
     } else {
-        for (int kb = ka; kb <= kz; ++kb) {
-            const int js = kb * BS + 32 * wid;
+        for (int kb = ka; kb <= kz; kb += STEP) {
+            const int js = kb * BS + 32 * sub;
             const int phys = phys_of(kb);
             if (phys < 0 || phys >= A.num_blocks) {
                 bad = true;
@@ -1269,8 +1286,8 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
             const bool brel = bias_on(C, js, A.R);
             typename KV::KReg kr[8];
             typename KV::template VRegs<DV> vs;
-            KV::k_sub(kr, kbase + base * DQK * KV::ESZ, wid, lane);
-            KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, wid, L - kb * BS, lane);
+            KV::k_sub(kr, kbase + base * DQK * KV::ESZ, sub, lane);
+            KV::template v_load<DV>(vs, vbase + base * DV * KV::ESZ, sub, L - kb * BS, lane);
             KV::template v_store<DV>(Vw, vs, lane);
             RelRegs rr;
             if (brel) rel_load(rr, C.relrow, C.pos, js, A.R, lane);
@@ -1286,11 +1303,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
         }
     }
 
-    // Merge the four waves' partial states through LDS.
+    // Merge the waves' partial states through LDS.
     __syncthreads();
-    float* Om = reinterpret_cast<float*>(smem);   // [4][32][DV]
-    float* Mm = Om + 4 * 32 * DV;                 // [4][32] reference max (or -inf)
-    float* Lm = Mm + 4 * 32;                      // [4][32] row sums
+    float* Om = reinterpret_cast<float*>(smem);   // [NW][32][DV]
+    float* Mm = Om + NW * 32 * DV;                // [NW][32] reference max (or -inf)
+    float* Lm = Mm + NW * 32;                     // [NW][32] row sums
     const float l_tot = C.l_sum + xor32(C.l_sum);
     const bool any_bad = __syncthreads_or(bad);
 #pragma unroll
@@ -1309,20 +1326,20 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     }
     __syncthreads();
 
-    for (int e = tid; e < 32 * DV; e += 256) {
+    for (int e = tid; e < 32 * DV; e += 64 * NW) {
         const int col = e / DV, dv = e % DV;
         const int cc = cg * 32 + col;
         if (cc >= ncols) continue;
-        float mw[4], M = -INFINITY;
+        float mw[NW], M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             mw[w] = Mm[w * 32 + col];
             M = fmaxf(M, mw[w]);
         }
         float den = 0.f, num = 0.f;
         if (M > -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const float f = __builtin_amdgcn_exp2f(mw[w] - M);  // exp2(-inf) = 0
                 den += f * Lm[w * 32 + col];
                 num += f * Om[(w * 32 + col) * DV + dv];
@@ -1340,6 +1357,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
 template <int DV, bool KV8>
 __global__ void __launch_bounds__(256, 2) decode_split_kernel(const DecodeArgs A) {
     decode_split_body<DV, KV8, false>(A);
+}
+
+template <int DV, bool KV8>
+__global__ void __launch_bounds__(512) decode_split8_kernel(const DecodeArgs A) {
+    decode_split_body<DV, KV8, false, 8>(A);
 }
 
 template <int DV>
@@ -1506,6 +1528,15 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
 
     typename KV::KReg kr[8];
     typename KV::template VRegs<DV> vs;
+    // bias values of the lane's 8 keys, loaded one block ahead (a clamped
+    // index keeps every read inside the row; out-of-range distances get 0)
+    auto rel_on = [&](int jsx) { return w_lo - (jsx + 31) < A.R; };
+    float rb[8];
+    auto rel_fetch = [&](int jsx) {
+        const int e0 = pos - (jsx + 8 * q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = relrow[min(max(e0 - i, 0), A.R - 1)];
+    };
     bool ok_cur = false;
     if (ka <= kz) {
         const size_t base = block_base(ka, ok_cur);
@@ -1513,12 +1544,14 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
             load_k16(kr, kel + base * DQK, wid, lane);
             KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base * DV), wid, L - ka * BS, lane);
         }
+        if (rel_on(ka * BS + 32 * wid)) rel_fetch(ka * BS + 32 * wid);
     }
 #pragma unroll 1
     for (int kb = ka; kb <= kz; ++kb) {
         const int js = kb * BS + 32 * wid;
         bool ok_next = false;
         const size_t base_next = kb < kz ? block_base(kb + 1, ok_next) : 0;
+        const bool brel_next = kb < kz && rel_on(js + BS);
         if (!ok_cur) {
             bad = true;
             if (ok_next) {
@@ -1526,6 +1559,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
                 KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base_next * DV), wid,
                                         L - (kb + 1) * BS, lane);
             }
+            if (brel_next) rel_fetch(js + BS);
             ok_cur = ok_next;
             continue;
         }
@@ -1543,7 +1577,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
         }
         if (ok_next) load_k16(kr, kel + base_next * DQK, wid, lane);
         // logits (log2 units, relative to the reference), bias, masks
-        const bool brel = w_lo - (js + 31) < A.R;
+        const bool brel = rel_on(js);
         const bool nmask = phantom || (js + 31 > w_lo) || (A.W > 0 && w_hi - js >= A.W);
         const int d0 = pos - (js + 8 * q);  // distance of the lane's key i is d0 - i
         float x[8];
@@ -1553,10 +1587,10 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int d = d0 - i;
-                const float rv = relrow[min(max(d, 0), A.R - 1)];
-                x[i] += (d >= 0 && d < A.R && pos >= 0) ? rv * l2f : 0.f;
+                x[i] += (d >= 0 && d < A.R && pos >= 0) ? rb[i] * l2f : 0.f;
             }
         }
+        if (brel_next) rel_fetch(js + BS);
         if (nmask) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1798,6 +1832,11 @@ hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
     if (dv == 128) {
         if (kv8) hipLaunchKernelGGL((decode_split_kernel<128, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((decode_split_kernel<128, false>), g, blk, 0, s, a);
+    } else if (a.wide && kv8) {
+        // at most one workgroup per CU: 8 waves each. (For bf16 K/V the
+        // second block in flight measured no faster, so the 4-wave kernel
+        // runs there.)
+        hipLaunchKernelGGL((decode_split8_kernel<64, true>), g, dim3(512), 0, s, a);
     } else {
         if (kv8) hipLaunchKernelGGL((decode_split_kernel<64, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((decode_split_kernel<64, false>), g, blk, 0, s, a);

@@ -68,16 +68,17 @@ def test_logpos_decode_small(case, splits):
     gpu_vs_oracle(b, what=f"{case} s{splits}", num_splits=splits)
 
 
-def test_logpos_one_is_the_plain_path_bitwise():
-    say("logit scale 1 == plain kernels")
+@pytest.mark.parametrize("splits", [3, 17])  # 2 x 8 x splits workgroups: one per CU, or more
+def test_logpos_one_is_the_plain_path_bitwise(splits):
+    say(f"logit scale 1 == plain kernels, {splits} splits")
     pre = W.make_prefill(55, [300], [500], 8, 2, 128, 256, 0).to(DEV)
     one = torch.ones(pre.rows, dtype=torch.float32, device=DEV)
     o1, l1 = run_prefill(pre, want_lse=True)
     o2, l2 = run_prefill(pre, want_lse=True, logit_scale=one)
     dec = W.make_decode(55, 2, 4, 64, 8, 64, 1024, 0, seq_lens=[900, 3000]).to(DEV)
     one = torch.ones(dec.rows, dtype=torch.float32, device=DEV)
-    d1, m1 = run_decode(dec, want_lse=True, num_splits=3)
-    d2, m2 = run_decode(dec, want_lse=True, num_splits=3, logit_scale=one)
+    d1, m1 = run_decode(dec, want_lse=True, num_splits=splits)
+    d2, m2 = run_decode(dec, want_lse=True, num_splits=splits, logit_scale=one)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(d1, d2) and torch.equal(m1, m2)

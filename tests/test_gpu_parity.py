@@ -102,6 +102,7 @@ DECODE_GRID = [
     (2, 4, [300, 1100], 16, 4, 128, 256, 0, None),      # G * n_q = 16: the 16-column kernel's limit
     (2, 5, [300, 1100], 16, 4, 64, 256, 0, None),       # G * n_q = 20: the 32-column kernel, one group
     (2, 4, [4, 1000], 16, 4, 128, 256, 0, None),        # a sequence holding only its n_q new tokens
+    (2, 4, [700, 4096], 64, 8, 64, 1024, 300, None),    # 32 columns, dv 64, window
 ]
 
 
@@ -124,6 +125,20 @@ def test_paged_decode_16_disjoint_workload():
     say("paged_decode_16x8k_128k_disjoint")
     _, mx, mean = gpu_vs_oracle(W.build("paged_decode_16x8k_128k_disjoint"), what="decode16 disjoint")
     say(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 17, 40])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_dv64_one_and_two_workgroups_per_cu(splits, fp8):
+    """The 32-column dv-64 decode over e4m3 K/V runs 8-wave workgroups (even
+    and odd blocks on two wave groups) when its grid fits one workgroup per
+    CU, else 4-wave ones, as over bf16 K/V: 2 x 8 x splits workgroups cross
+    256 between 5 and 17 splits. Odd block counts per split leave the
+    odd-block waves one block short, and the 700-token sequence leaves some
+    splits empty."""
+    say(f"decode dv64 splits={splits} fp8={fp8}")
+    b = W.make_decode(41, 2, 4, 64, 8, 64, 1024, 0, seq_lens=[700, 4096], kv_fp8=fp8)
+    gpu_vs_oracle(b, what=f"dv64 s{splits} fp8{int(fp8)}", num_splits=splits)
 
 
 @pytest.mark.parametrize("name", ["verify_decode_b1_100k", "verify_decode_b8_100k"])
@@ -398,11 +413,13 @@ def test_graph_capture_replay():
         run_prefill(W.make_prefill(1, [64], [0], 4, 1, 128, 128, 0).to(DEV))   # eager work between
 
 
-def test_invalid_block_id_gives_nan_not_a_fault():
-    say("invalid block id")
-    b = W.make_decode(3, 2, 1, 8, 2, 128, 64, 0, seq_lens=[500, 600])
+@pytest.mark.parametrize("shape", [(1, 8, 2, 128), (4, 64, 8, 64)], ids=["4col_dv128", "32col_dv64"])
+def test_invalid_block_id_gives_nan_not_a_fault(shape):
+    n_q, Hq, Hkv, dv = shape
+    say(f"invalid block id {shape}")
+    b = W.make_decode(3, 2, n_q, Hq, Hkv, dv, 64, 0, seq_lens=[500, 600])
     b.block_tables[1, 2] = 10_000          # out of range for this pool
     out, _ = run_decode(b.to(DEV))
-    out = out.cpu()
+    out = out.cpu().view(2, n_q, Hq, dv)   # [sequence, token, head, dv]
     assert torch.isnan(out[1]).all()
     assert torch.isfinite(out[0]).all()
