@@ -103,6 +103,8 @@ DECODE_GRID = [
     (2, 5, [300, 1100], 16, 4, 64, 256, 0, None),       # G * n_q = 20: the 32-column kernel, one group
     (2, 4, [4, 1000], 16, 4, 128, 256, 0, None),        # a sequence holding only its n_q new tokens
     (2, 4, [700, 4096], 64, 8, 64, 1024, 300, None),    # 32 columns, dv 64, window
+    (2, 3, [700, 3000], 64, 2, 64, 1024, 0, None),      # G = 32, 96 columns: three column groups
+    (3, 2, [130, 900, 2600], 64, 2, 128, 256, 384, None),  # 64 columns: two column groups, dv 128, window
 ]
 
 
@@ -158,6 +160,7 @@ FP8_GRID = [
     (2, 4, [700, 4096], 64, 8, 64, 1024, 0),           # G * n_q = 32: 32-column kernel with prefetch
     (2, 8, [900, 2000], 48, 8, 128, 512, 0),           # 48 columns, dv 128: two groups, no prefetch
     (4, 3, [3, 250, 520, 1300], 16, 4, 128, 256, 300), # window; a sequence shorter than a block
+    (2, 4, [700, 2000], 64, 4, 64, 1024, 0),           # 64 columns, dv 64: two column groups
 ]
 
 
