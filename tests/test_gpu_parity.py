@@ -105,6 +105,7 @@ DECODE_GRID = [
     (2, 4, [700, 4096], 64, 8, 64, 1024, 300, None),    # 32 columns, dv 64, window
     (2, 3, [700, 3000], 64, 2, 64, 1024, 0, None),      # G = 32, 96 columns: three column groups
     (3, 2, [130, 900, 2600], 64, 2, 128, 256, 384, None),  # 64 columns: two column groups, dv 128, window
+    (1, 16, [2000], 128, 8, 64, 1024, 0, None),         # G * n_q = 256, the largest accepted: 8 groups
 ]
 
 
