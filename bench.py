@@ -247,7 +247,7 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="time one named workload on its own (a report line, not the step line)")
     ap.add_argument("--no-flush", action="store_true",
-                    help="with --workload: skip the 1 GiB cache-evicting write between timed calls")
+                    help="with --workload: skip the 1 GiB cache-evicting read between timed calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
