@@ -324,18 +324,15 @@ __device__ __forceinline__ void softmax_pv(Cols<DV>& C, const f32x16& s, bool ha
     }
 }
 
+// The lane's query operands. A column past the last real one points at a
+// real row (its logits are masked and its output is never stored), so the
+// loads need no branch, and no wait is forced on them before the loads that
+// follow.
 template <int DV>
-__device__ __forceinline__ void load_q(Cols<DV>& C, const uint16_t* qrow, bool real, int lane) {
+__device__ __forceinline__ void load_q(Cols<DV>& C, const uint16_t* qrow, int lane) {
     const int hh = lane >> 5;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        if (real) {
-            C.qreg[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hh);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) C.qreg[st][i] = (__bf16)0.f;
-        }
-    }
+    for (int st = 0; st < 8; ++st) C.qreg[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hh);
 }
 
 template <int DV>
@@ -586,7 +583,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     C.w_lo = ctx + qa;
     C.w_hi = ctx + qb;
     C.phantom = qb < qa + 31;
-    load_q(C, A.q + trow * DQK, real, lane);
+    load_q(C, A.q + trow * DQK, lane);
     init_acc(C);
 
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
@@ -826,7 +823,7 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
         load_p(pv0, js_lo - 32);
         load_p(pv, js_lo);
     }
-    load_q(C, A.q + trow * DQK, real, lane);
+    load_q(C, A.q + trow * DQK, lane);
 #pragma unroll
     for (int st = 0; st < DR / 16; ++st) {
         if (real) {
@@ -1168,6 +1165,11 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     const int cg = id % A.n_cg;
     const int split = id / A.n_cg;
 
+    // With no window a split's first block does not depend on the sequence
+    // length, so its block-table slice is requested before that arrives.
+    const int tab_spec_lo = split * A.bps + par;
+    const int* const tab_row = A.tables + (long long)b * A.max_blocks;
+    const int tab_spec = (A.W == 0 && tab_spec_lo + lane < A.max_blocks) ? tab_row[tab_spec_lo + lane] : -1;
     const int L = A.seq_lens[b];
     const int ncols = A.G * A.n_q;
     const int c = cg * 32 + n;
@@ -1186,7 +1188,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     C.w_lo = L - A.n_q + (cg * 32) / A.G;
     C.w_hi = L - A.n_q + c_hi / A.G;
     C.phantom = c_hi < cg * 32 + 31;
-    load_q(C, A.q + trow * DQK, real, lane);
+    load_q(C, A.q + trow * DQK, lane);
     init_acc(C);
 
     const int nb = (L + BS - 1) / BS;
@@ -1195,7 +1197,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     const int s_hi = min(s_lo + A.bps, nb);
     __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Lds::WAVE);
     float* Rw = reinterpret_cast<float*>(smem + wid * Lds::WAVE + Lds::V_BYTES);
-    const int* tab = A.tables + (long long)b * A.max_blocks;
+    const int* tab = tab_row;
     bool bad = false;
 
     // This wave's subtiles that are not entirely masked form one run of
@@ -1206,7 +1208,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
 
     // split's block-table slice, lane i = entry tab_base + i
     int tab_base = ka;
-    int tabv = (ka + lane <= kz) ? tab[ka + lane] : -1;
+    int tabv = (ka + lane <= kz) ? (A.W == 0 && ka == tab_spec_lo ? tab_spec : tab[ka + lane]) : -1;
     auto phys_of = [&](int kb) {
         if (kb - tab_base >= 64) {
             tab_base += 64;
@@ -1471,6 +1473,11 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     id /= A.batch;
     const int split = id / A.n_cg;  // n_cg == 1 for this variant
 
+    // With no window a split's first block does not depend on the sequence
+    // length, so its block-table slice is requested before that arrives.
+    const int tab_spec_lo = split * A.bps;
+    const int* const tab_row = A.tables + (long long)b * A.max_blocks;
+    const int tab_spec = (A.W == 0 && tab_spec_lo + lane < A.max_blocks) ? tab_row[tab_spec_lo + lane] : -1;
     const int L = A.seq_lens[b];
     const int ncols = A.G * A.n_q;
     const bool real = c < ncols;
@@ -1486,15 +1493,9 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     const bool phantom = ncols < 16;
 
     bf16x8 qreg[4];
+    // as load_q: a column past the last real one reads a real row
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        if (real) {
-            qreg[st] = *reinterpret_cast<const bf16x8*>(A.q + trow * DQK + 32 * st + 8 * q);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qreg[st][i] = (__bf16)0.f;
-        }
-    }
+    for (int st = 0; st < 4; ++st) qreg[st] = *reinterpret_cast<const bf16x8*>(A.q + trow * DQK + 32 * st + 8 * q);
     f32x4v O[DV / 16];
 #pragma unroll
     for (int t = 0; t < DV / 16; ++t) O[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
@@ -1506,7 +1507,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     const int s_lo = kb_first + split * A.bps;
     const int s_hi = min(s_lo + A.bps, nb);
     __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Decode16Lds<DV>::V_BYTES);
-    const int* tab = A.tables + (long long)b * A.max_blocks;
+    const int* tab = tab_row;
     bool bad = false;
 
     auto masked_all16 = [&](int js) { return js > w_hi || (A.W > 0 && w_lo - (js + 31) >= A.W); };
@@ -1515,7 +1516,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     while (kz >= ka && masked_all16(kz * BS + 32 * wid)) --kz;
 
     int tab_base = ka;
-    int tabv = (ka + lane <= kz) ? tab[ka + lane] : -1;
+    int tabv = (ka + lane <= kz) ? (A.W == 0 && ka == tab_spec_lo ? tab_spec : tab[ka + lane]) : -1;
     auto block_base = [&](int kb, bool& okk) -> size_t {
         if (kb - tab_base >= 64) {
             tab_base += 64;
