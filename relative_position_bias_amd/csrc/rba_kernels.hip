@@ -1530,7 +1530,10 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     typename KV::KReg kr[8];
     typename KV::template VRegs<DV> vs;
     // bias values of the lane's 8 keys, loaded one block ahead (a clamped
-    // index keeps every read inside the row; out-of-range distances get 0)
+    // index keeps every read inside the row; out-of-range distances get 0).
+    // The log-position variant has no registers to spare for that: there
+    // they are loaded in the block's own step.
+    constexpr bool REL_AHEAD = !LS;
     auto rel_on = [&](int jsx) { return w_lo - (jsx + 31) < A.R; };
     float rb[8];
     auto rel_fetch = [&](int jsx) {
@@ -1545,7 +1548,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
             load_k16(kr, kel + base * DQK, wid, lane);
             KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base * DV), wid, L - ka * BS, lane);
         }
-        if (rel_on(ka * BS + 32 * wid)) rel_fetch(ka * BS + 32 * wid);
+        if (REL_AHEAD && rel_on(ka * BS + 32 * wid)) rel_fetch(ka * BS + 32 * wid);
     }
 #pragma unroll 1
     for (int kb = ka; kb <= kz; ++kb) {
@@ -1560,7 +1563,7 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
                 KV::template v_load<DV>(vs, reinterpret_cast<const char*>(vel + base_next * DV), wid,
                                         L - (kb + 1) * BS, lane);
             }
-            if (brel_next) rel_fetch(js + BS);
+            if (REL_AHEAD && brel_next) rel_fetch(js + BS);
             ok_cur = ok_next;
             continue;
         }
@@ -1585,13 +1588,14 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = S[i >> 2][i & 3] * c1f - m_ref;
         if (brel) {
+            if (!REL_AHEAD) rel_fetch(js);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int d = d0 - i;
                 x[i] += (d >= 0 && d < A.R && pos >= 0) ? rb[i] * l2f : 0.f;
             }
         }
-        if (brel_next) rel_fetch(js + BS);
+        if (REL_AHEAD && brel_next) rel_fetch(js + BS);
         if (nmask) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
