@@ -589,7 +589,22 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
     const int kb_hi = i_hi / BS;
-    const int js_end = kb_hi * BS + 3 * 32;  // last subtile start
+    // Block order. A windowed tile spans a few blocks, most of them shared
+    // with its neighbours. Each such tile walks its blocks as a rotation that
+    // starts at its first block whose index is a multiple of RM, the block
+    // count of a tile aligned to the blocks: the tiles with RM blocks then
+    // all read block b at their step b mod RM, at the same time, so a block
+    // that L2 holds for one of them is still there for the others (between
+    // steps the bias streaming through L2 would evict it). Without a window,
+    // or for a span of 64 blocks or more, the order is ascending.
+    int kb_first = kb_lo;
+    if (WIN && kb_hi - kb_lo < 64) {
+        const int RM = (A.W + A.QT - 1 + BS - 1) / BS;
+        const int b0 = kb_lo + (RM - kb_lo % RM) % RM;
+        if (b0 <= kb_hi) kb_first = b0;
+    }
+    const int kb_last = kb_first > kb_lo ? kb_first - 1 : kb_hi;
+    auto next_kb = [&](int kb) { return kb == kb_hi ? kb_lo : kb + 1; };
     const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
@@ -624,11 +639,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
 
     bool ok = false;
     {
-        const size_t base = block_base(kb_lo, ok);
-        if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, wid, lane);
+        const size_t base = block_base(kb_first, ok);
+        if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_first * BS, wid, lane);
     }
     RelVals rv[2];  // bias of the current and of the next subtile
-    if (rel_active(kb_lo * BS)) rel_fetch(rv[0], C.relrow, C.pos, kb_lo * BS, A.R, rel_inside(kb_lo * BS), lane);
+    if (rel_active(kb_first * BS))
+        rel_fetch(rv[0], C.relrow, C.pos, kb_first * BS, A.R, rel_inside(kb_first * BS), lane);
 
     // One block: wait for its copy, start the next block's copy into the
     // other buffers (every wave left them at this barrier), compute.
@@ -637,9 +653,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
         lds_barrier();
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
-        if (kb < kb_hi) {
-            const size_t base = block_base(kb + 1, ok);
-            if (ok) kv_dma<DV, NW>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - (kb + 1) * BS, wid, lane);
+        const int kbn = kb != kb_last ? next_kb(kb) : -1;  // the next block, if any
+        if (kbn >= 0) {
+            const size_t base = block_base(kbn, ok);
+            if (ok) kv_dma<DV, NW>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - kbn * BS, wid, lane);
         }
         if (!wave_active) return;
 #pragma unroll
@@ -651,8 +668,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
             // before it, so a request placed ahead of it would be waited for
             // too.
             auto prefetch_rel = [&]() {
-                if (js + 32 <= js_end && rel_active(js + 32))
-                    rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, js + 32, A.R, rel_inside(js + 32), lane);
+                const int jn = sub < 3 ? js + 32 : (kbn >= 0 ? kbn * BS : -1);  // the next subtile
+                if (jn >= 0 && rel_active(jn))
+                    rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, jn, A.R, rel_inside(jn), lane);
             };
             auto scores = [&](float(&x)[16]) {
                 const f32x16 s = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
@@ -690,11 +708,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
             }
         }
     };
-    for (int kb = kb_lo;;) {
+    for (int kb = kb_first;;) {
         step(K0, V0, K1, V1, kb);
-        if (++kb > kb_hi) break;
+        if (kb == kb_last) break;
+        kb = next_kb(kb);
         step(K1, V1, K0, V0, kb);
-        if (++kb > kb_hi) break;
+        if (kb == kb_last) break;
+        kb = next_kb(kb);
     }
 
     if (!wave_active || !real) return;

@@ -70,7 +70,14 @@ def test_relproj_small(case):
 def test_relproj_equals_materialised_bias(case):
     """The same call through rba_prefill with rel formed by the oracle
     (float64, rounded to fp32): the two kernels differ only in how the bias
-    reaches the scores, so they agree far inside the parity bar."""
+    reaches the scores, so they agree far inside the parity bar. Without a
+    window both visit the keys in the same order and agree to fp32 rounding
+    (2e-4). With one, rba_prefill walks a tile's blocks as a rotation (for L2
+    reuse between neighbouring tiles) while the in-kernel-bias kernel walks
+    them in ascending order; P is rounded to bf16 relative to a running
+    reference that then differs, so the bound is the bf16 rounding of P:
+    relative error <= 2^-9 per weight, at most ~2^-8 * max|v| on an output,
+    far less on average. lse is built from fp32 sums either way."""
     q_lens, ctx, Hq, Hkv, dv, R, Wn, Hp = case
     say(f"relproj vs rel {case}")
     b_cpu = W.make_prefill(29, q_lens, ctx, Hq, Hkv, dv, R, Wn, d_r=64, proj_heads=Hp)
@@ -82,10 +89,16 @@ def test_relproj_equals_materialised_bias(case):
                          want_lse=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o1).all()
-    d = (o1 - o2).abs().max().item()
+    diff = (o1 - o2).abs()
+    d, dm = diff.max().item(), diff.mean().item()
     dl = (l1 - l2).abs().max().item()
-    say(f"  max |relproj - rel| {d:.3e}, lse {dl:.3e}")
-    assert d <= 2e-4 and dl <= 2e-5
+    say(f"  max |relproj - rel| {d:.3e}, mean {dm:.3e}, lse {dl:.3e}")
+    if Wn == 0:
+        assert d <= 2e-4
+    else:
+        vmax = float(b_cpu.v_cache.float().nan_to_num(0).abs().max())
+        assert d <= 2.0 ** -8 * vmax and dm <= 2e-4
+    assert dl <= 2e-5
 
 
 def test_shared_projection_equals_replicated_per_head():
