@@ -44,14 +44,21 @@
  *     that returns an error has enqueued nothing and written nothing.
  *   - Return 0 on success or a negative RBA_ERR_* code; rba_last_error()
  *     then describes the problem (thread-local).
+ *   - Alignment: q, k_cache, v_cache, out, workspace, r and rel_proj must be
+ *     16-byte aligned; rel, lse, cu_q, seq_lens, block_tables, sink, gate and
+ *     logit_scale 4-byte aligned (RBA_ERR_UNSUPPORTED otherwise).
  *   - Values the library cannot check without reading device memory are the
- *     caller's contract (undefined results, never out-of-bounds accesses, if
- *     violated): q_len_b <= seq_lens[b] <= max_seq_len, cu_q non-decreasing,
- *     and q_len_b <= max_q_len. Table entries for blocks a query can see must
- *     be in [0, num_blocks); an entry outside that range makes the affected
- *     rows NaN instead of being dereferenced. Entries for blocks that no query
- *     of the call can see (wholly outside every window) are never read and
- *     may hold anything, e.g. -1.
+ *     caller's contract: q_len_b <= seq_lens[b] <= max_seq_len, cu_q
+ *     non-decreasing with cu_q[batch] = the rows of q, and q_len_b <=
+ *     max_q_len. A seq_lens[b] below q_len_b (or n_q), above what the
+ *     block-table row addresses (max_blocks_per_seq * 128), or (decode) above
+ *     what the split plan for max_seq_len covers makes sequence b's rows NaN;
+ *     no block-table entry past the row is read. Table entries for blocks a
+ *     query can see must be in [0, num_blocks); an entry outside that range
+ *     makes the affected rows NaN instead of being dereferenced. Entries for
+ *     blocks that no query of the call can see (wholly outside every window)
+ *     are never read and may hold anything, e.g. -1. Other violations give
+ *     undefined results, never out-of-bounds accesses.
  *   - Slots of the last block past seq_lens[b] are never used: whatever they
  *     hold (NaN included) contributes exactly 0.
  */
@@ -81,8 +88,8 @@ typedef struct rba_attn_params {
                            /* h / (Hq / Hkv)                                         */
     int32_t head_dim_qk;   /* must be 128                                            */
     int32_t head_dim_v;    /* 64 or 128                                              */
-    int32_t rel_extent;    /* R: bias defined for distances 0 <= i-j < R, 0 beyond;  */
-                           /* R >= 4 and R % 4 == 0                                  */
+    int32_t rel_extent;    /* R >= 1: bias defined for distances 0 <= i-j < R, 0     */
+                           /* beyond                                                 */
     int32_t window;        /* W: 0 = no window; else key visible iff 0 <= i-j < W    */
     float scale;           /* finite multiplier of q.k (e.g. 1/sqrt(128))            */
     int32_t block_size;    /* must be RBA_BLOCK_SIZE                                 */

@@ -138,6 +138,71 @@ def attend(q, k, v, rel, q_lens, seq_lens, *, rel_extent, window, scale,
     return out, lse
 
 
+def attend_rows_dense(q, k, v, rel, positions, *, rel_extent, window, scale, sink=None, gate=None,
+                      logit_scale=None, group=32):
+    """The same definition as ``attend``, for selected query rows of ONE
+    sequence, written as dense float64 matrices: per group of rows and per
+    head, the score matrix is one matmul, and the mask and the bias are
+    explicit matrices indexed by the distance i - j. Used to check many
+    sampled rows of long sequences, where the loop form needs seconds per
+    row. It follows the same passages as ``attend`` (oracle.c lists them):
+    visible keys j <= i and, with a window, i - j < W; bias rel[t, h, i - j]
+    for distances below the extent and 0 beyond; softmax over the visible
+    keys; out = softmax-weighted sum of V; lse = log of the normaliser.
+
+    q     [n, Hq, dqk]   the selected query rows
+    k, v  [L, Hkv, dqk], [L, Hkv, dv]   the sequence's keys/values in order
+    rel   [n, Hq, R]     the bias rows of the selected queries
+    positions  [n] absolute positions i of the rows (0 <= i < L)
+    sink, gate, logit_scale  optional [n, Hq], [n, Hq], [n] (as ``attend``)
+    Returns (out [n, Hq, dv], lse [n, Hq]) in float64.
+    """
+    q, k, v, rel = _f64(q), _f64(k), _f64(v), _f64(rel)
+    pos = np.asarray(positions, dtype=np.int64).reshape(-1)
+    n, Hq, _ = q.shape
+    L, Hkv, dv = v.shape
+    R = rel.shape[2]
+    if R != rel_extent or k.shape[0] != L or pos.shape[0] != n:
+        raise ValueError("shapes do not match")
+    if n and (pos.min() < 0 or pos.max() >= L):
+        raise ValueError("positions must lie in [0, L)")
+    if logit_scale is not None:
+        f = _f64(logit_scale).reshape(-1)
+        q = q * f[:, None, None]
+        rel = rel * f[:, None, None]
+    G = Hq // Hkv
+    out = np.empty((n, Hq, dv))
+    lse = np.empty((n, Hq))
+    for a in range(0, n, group):
+        sel = slice(a, min(a + group, n))
+        p = pos[sel]
+        kv_len = int(p.max()) + 1
+        dist = p[:, None] - np.arange(kv_len)[None, :]          # i - j
+        visible = dist >= 0
+        if window > 0:
+            visible &= dist < window
+        in_extent = (dist >= 0) & (dist < R)
+        d_idx = np.clip(dist, 0, R - 1)
+        for h in range(Hq):
+            g = h // G
+            S = q[sel, h] @ k[:kv_len, g].T
+            B = np.where(in_extent, np.take_along_axis(rel[sel, h], d_idx, axis=1), 0.0)
+            X = np.where(visible, scale * S + B, -np.inf)
+            m = X.max(axis=1)
+            if sink is not None:
+                m = np.maximum(m, _f64(sink)[sel, h])
+            P = np.exp(X - m[:, None])
+            den = P.sum(axis=1)
+            if sink is not None:
+                den = den + np.exp(_f64(sink)[sel, h] - m)
+            o = (P @ v[:kv_len, g]) / den[:, None]
+            if gate is not None:
+                o = o / (1.0 + np.exp(-_f64(gate)[sel, h]))[:, None]
+            out[sel, h] = o
+            lse[sel, h] = m + np.log(den)
+    return out, lse
+
+
 def rel_from_proj(r, proj):
     """The bias tensor from the R branch: rel = r @ rel_logits_proj.
 
@@ -169,7 +234,9 @@ def rel_from_proj(r, proj):
 def unpage(cache, block_tables, seq_lens, block_size=128):
     """Gather a paged cache [num_blocks, H, block_size, d] into contiguous
     per-sequence rows [sum(seq_lens), H, d] (sequence b: logical block n is
-    physical block block_tables[b][n], slot s is position n*block_size + s)."""
+    physical block block_tables[b][n], slot s is position n*block_size + s).
+    Key positions are block ordinal times the block size plus the slot
+    ("Inkling-Small on Gaudi 2", "Attention with a relative bias")."""
     cache = np.asarray(cache)
     parts = []
     for b, L in enumerate(seq_lens):

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 
 #include "rba.h"
@@ -48,9 +50,6 @@ int check_params(const rba_attn_params* p) {
     if (p->head_dim_v != 64 && p->head_dim_v != 128)
         return fail(RBA_ERR_UNSUPPORTED, "head_dim_v %d unsupported (64 or 128)", p->head_dim_v);
     if (p->rel_extent < 1) return fail(RBA_ERR_SHAPE, "rel_extent %d must be >= 1", p->rel_extent);
-    if (p->rel_extent % 4 != 0)
-        return fail(RBA_ERR_UNSUPPORTED, "rel_extent %d unsupported (must be a multiple of 4)",
-                    p->rel_extent);
     if (p->window < 0) return fail(RBA_ERR_SHAPE, "window %d must be >= 0", p->window);
     if (!isfinite(p->scale)) return fail(RBA_ERR_SHAPE, "scale is not finite");
     if (p->block_size != RBA_BLOCK_SIZE)
@@ -81,23 +80,26 @@ int prefill_hpw(int G) {
     return 1;
 }
 
+// CU count of the current device, queried once per device. Any thread may
+// fill an entry; every filler stores the same value, and the atomics make the
+// concurrent first calls race-free.
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return 256;
     }
-    if (cached[dev] == 0) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0) {
             (void)hipGetLastError();
             cus = 256;
         }
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
 
 int64_t decode_nb_eff(const rba_attn_params* p, int32_t n_q, int32_t max_seq_len) {
@@ -162,7 +164,7 @@ int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cach
                      int32_t num_blocks, const void* rel, const int32_t* cu_q, const int32_t* seq_lens,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch,
                      int32_t max_q_len, int32_t max_seq_len, const float* out, const float* lse,
-                     bool* nothing, const char* rel_name = "rel") {
+                     bool* nothing, const char* rel_name = "rel", bool rel_is_r = false) {
     *nothing = false;
     int rc = check_params(p);
     if (rc) return rc;
@@ -178,8 +180,12 @@ int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cach
     if (cu_q == nullptr || seq_lens == nullptr) return fail(RBA_ERR_NULL, "cu_q/seq_lens is NULL");
     rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
     if (rc) return rc;
-    if (!aligned16(q) || !aligned16(rel) || !aligned16(out))
-        return fail(RBA_ERR_UNSUPPORTED, "q/%s/out must be 16-byte aligned", rel_name);
+    if (!aligned16(q) || !aligned16(out))
+        return fail(RBA_ERR_UNSUPPORTED, "q/out must be 16-byte aligned");
+    // fp32 rel rows start at any multiple of R floats: 4-byte alignment; the
+    // bf16 r vectors of the in-kernel producer are read 16 bytes at a time
+    if (rel_is_r ? !aligned16(rel) : !aligned4(rel))
+        return fail(RBA_ERR_UNSUPPORTED, "%s must be %d-byte aligned", rel_name, rel_is_r ? 16 : 4);
     if (!aligned4(cu_q) || !aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
         return fail(RBA_ERR_UNSUPPORTED, "cu_q/seq_lens/lse must be 4-byte aligned");
     const int G = p->num_heads_q / p->num_heads_kv;
@@ -211,8 +217,9 @@ int validate_decode(const rba_attn_params* p, const void* q, const void* k_cache
     if (need_out && out == nullptr) return fail(RBA_ERR_NULL, "out is NULL");
     rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
     if (rc) return rc;
-    if (!aligned16(q) || !aligned16(rel) || (need_out && !aligned16(out)))
-        return fail(RBA_ERR_UNSUPPORTED, "q/rel/out must be 16-byte aligned");
+    if (!aligned16(q) || (need_out && !aligned16(out)))
+        return fail(RBA_ERR_UNSUPPORTED, "q/out must be 16-byte aligned");
+    if (!aligned4(rel)) return fail(RBA_ERR_UNSUPPORTED, "rel must be 4-byte aligned");
     if (!aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
         return fail(RBA_ERR_UNSUPPORTED, "seq_lens/lse must be 4-byte aligned");
     const int32_t splits = num_splits ? num_splits : plan_splits(p, batch, n_q, max_seq_len, device_cus());
@@ -368,7 +375,8 @@ int rba_prefill_relproj(const rba_attn_params* params, const void* q, const void
     if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
     bool nothing;
     int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
-                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r");
+                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r",
+                              true);
     if (rc || nothing) return rc;
     if (d_r != 64) return fail(RBA_ERR_UNSUPPORTED, "d_r %d: only 64 is supported", d_r);
     if (proj_heads != 1 && proj_heads != params->num_heads_q)

@@ -174,8 +174,14 @@ __device__ __forceinline__ bool bias_on(const Cols<DV>& C, int js, int R) {
 
 // rel pieces one 32-key subtile needs for this lane's own row: row n needs
 // rel[t_n, h_n, a_n .. a_n + 36) with a_n = floor4(pos_n - js - 31); lane
-// (n, hh) holds the float4 pieces c4 = hh, hh + 2, ... < 9. Pieces outside
-// [0, R) are zeros (distance >= R has bias 0, distance < 0 is masked).
+// (n, hh) holds the float4 pieces c4 = hh, hh + 2, ... < 9. Entries at
+// distances >= R are zeros (bias 0 there), pieces below distance 0 too (those
+// keys are masked). A piece wholly inside [0, R) is one 16-byte load at
+// 4-byte alignment (a row starts at a multiple of R floats); the one piece
+// that holds distance R - 1 when R is not a multiple of 4 is read element by
+// element.
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
 struct RelRegs {
     f32x4 r[5];
 };
@@ -188,7 +194,14 @@ __device__ __forceinline__ void rel_load(RelRegs& v, const float* relrow, int po
         const int c4 = hh + 2 * k;
         const int a = a_n + 4 * c4;
         v.r[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c4 < 9 && pos >= 0 && a >= 0 && a + 4 <= R) v.r[k] = *reinterpret_cast<const f32x4*>(relrow + a);
+        if (c4 < 9 && pos >= 0 && a >= 0) {
+            if (a + 4 <= R) {
+                v.r[k] = *reinterpret_cast<const f32x4u*>(relrow + a);
+            } else if (a < R) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v.r[k][e] = a + e < R ? relrow[a + e] : 0.f;
+            }
+        }
     }
 }
 
@@ -482,8 +495,6 @@ struct RelVals {
     float v[16];
 };
 
-typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
-
 __device__ __forceinline__ void rel_fetch(RelVals& rv, const float* relrow, int pos, int js, int R, bool inside,
                                           int lane) {
     const int hh = lane >> 5;
@@ -585,6 +596,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     C.phantom = qb < qa + 31;
     load_q(C, A.q + trow * DQK, lane);
     init_acc(C);
+    // A device length that breaks the caller's contract (fewer keys than new
+    // rows, or more keys than the block-table row can address) makes the
+    // tile's rows NaN; no table entry past the row is ever read.
+    if (ctx < 0 || (long long)L > (long long)A.max_blocks * BS) {
+        if (wave_active && real)
+            store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, true, -INFINITY, INFINITY, lane);
+        return;
+    }
 
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
@@ -854,6 +873,14 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
         }
     }
     init_acc(C);
+    // A device length that breaks the caller's contract (fewer keys than new
+    // rows, or more keys than the block-table row can address) makes the
+    // tile's rows NaN; no table entry past the row is ever read.
+    if (ctx < 0 || (long long)L > (long long)A.max_blocks * BS) {
+        if (wave_active && real)
+            store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, true, -INFINITY, INFINITY, lane);
+        return;
+    }
     bool bad = false;
 
     int tab_base = kb_lo;
@@ -1211,14 +1238,19 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     load_q(C, A.q + trow * DQK, lane);
     init_acc(C);
 
-    const int nb = (L + BS - 1) / BS;
+    const int nb = L / BS + (L % BS != 0);
     const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
     const int s_lo = kb_first + split * A.bps;
-    const int s_hi = min(s_lo + A.bps, nb);
+    // A device length that breaks the caller's contract (fewer keys than
+    // query tokens, more than the block-table row addresses, or more than the
+    // split plan made from the host's max_seq_len covers) gives NaN rows; no
+    // table entry past the row is read.
+    const bool len_bad = L < A.n_q || nb > A.max_blocks || nb > kb_first + A.splits * A.bps;
+    const int s_hi = len_bad ? s_lo : min(s_lo + A.bps, nb);
     __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Lds::WAVE);
     float* Rw = reinterpret_cast<float*>(smem + wid * Lds::WAVE + Lds::V_BYTES);
     const int* tab = tab_row;
-    bool bad = false;
+    bool bad = len_bad;
 
     // This wave's subtiles that are not entirely masked form one run of
     // blocks ka, ka + STEP, ..., kz.
@@ -1522,13 +1554,18 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     float m_ref = 0.f, l_sum = 0.f;
     bool m_set = false;
 
-    const int nb = (L + BS - 1) / BS;
+    const int nb = L / BS + (L % BS != 0);
     const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
     const int s_lo = kb_first + split * A.bps;
-    const int s_hi = min(s_lo + A.bps, nb);
+    // A device length that breaks the caller's contract (fewer keys than
+    // query tokens, more than the block-table row addresses, or more than the
+    // split plan made from the host's max_seq_len covers) gives NaN rows; no
+    // table entry past the row is read.
+    const bool len_bad = L < A.n_q || nb > A.max_blocks || nb > kb_first + A.splits * A.bps;
+    const int s_hi = len_bad ? s_lo : min(s_lo + A.bps, nb);
     __bf16* Vw = reinterpret_cast<__bf16*>(smem + wid * Decode16Lds<DV>::V_BYTES);
     const int* tab = tab_row;
-    bool bad = false;
+    bool bad = len_bad;
 
     auto masked_all16 = [&](int js) { return js > w_hi || (A.W > 0 && w_lo - (js + 31) >= A.W); };
     int ka = s_lo, kz = s_hi - 1;

@@ -144,6 +144,23 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _shape(t: Optional[torch.Tensor], shape, name: str) -> None:
+    """Raise unless tensor t (if given) has exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _cache_shapes(q, k_cache, v_cache, block_tables, batch):
+    """q [rows, Hq, 128]; caches [nb, Hkv, 128, 128] / [nb, Hkv, 128, dv];
+    block_tables [>= batch, max_blocks]."""
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be 3-D and k_cache / v_cache 4-D")
+    if v_cache.shape[:3] != k_cache.shape[:3] or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("k_cache [nb, Hkv, 128, dqk] and v_cache [nb, Hkv, 128, dv] disagree with q")
+    if block_tables.dim() != 2 or block_tables.shape[0] < batch:
+        raise ValueError("block_tables must be [batch, max_blocks]")
+
+
 def _opt(t: Optional[torch.Tensor], name: str, shape) -> Optional[int]:
     """Device pointer of an optional fp32 [rows, Hq] input (sink / gate)."""
     if t is None:
@@ -151,6 +168,17 @@ def _opt(t: Optional[torch.Tensor], name: str, shape) -> Optional[int]:
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must be {list(shape)}")
     return _dev(t, torch.float32, name)
+
+
+def _prefill_batch(cu_q, seq_lens) -> int:
+    """Sequence count of a prefill call: cu_q holds batch + 1 offsets and
+    seq_lens one length per sequence."""
+    if cu_q.dim() != 1 or cu_q.numel() < 1:
+        raise ValueError("cu_q must hold batch + 1 offsets")
+    batch = cu_q.numel() - 1
+    if seq_lens.numel() != batch:
+        raise ValueError(f"seq_lens must have {batch} entries (cu_q.numel() - 1)")
+    return batch
 
 
 def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: int, scale: float,
@@ -169,15 +197,16 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
     R = rel.shape[2]
-    if rel.shape[:2] != (total_q, Hq):
+    if rel.dim() != 3 or rel.shape[:2] != (total_q, Hq):
         raise ValueError("rel must be [total_q, Hq, R]")
-    if block_tables.dim() != 2:
-        raise ValueError("block_tables must be 2-D")
-    batch = cu_q.numel() - 1
+    batch = _prefill_batch(cu_q, seq_lens)
+    _cache_shapes(q, k_cache, v_cache, block_tables, batch)
     if out is None:
         out = torch.empty((total_q, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _shape(out, (total_q, Hq, dv), "out")
+    _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
     if logit_scale is not None:
         if sink is not None or gate is not None:
@@ -229,13 +258,14 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
     if proj.dim() != 3 or proj.shape[2] != d_r:
         raise ValueError("proj must be [proj_heads, R, d_r]")
     proj_heads, R = proj.shape[0], proj.shape[1]
-    if block_tables.dim() != 2:
-        raise ValueError("block_tables must be 2-D")
-    batch = cu_q.numel() - 1
+    batch = _prefill_batch(cu_q, seq_lens)
+    _cache_shapes(q, k_cache, v_cache, block_tables, batch)
     if out is None:
         out = torch.empty((total_q, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _shape(out, (total_q, Hq, dv), "out")
+    _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
     _check(lib().rba_prefill_relproj(
         ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
@@ -278,6 +308,7 @@ def _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q, window
     batch = rows // n_q
     if seq_lens.numel() != batch:
         raise ValueError("seq_lens must have batch entries")
+    _cache_shapes(q, k_cache, v_cache, block_tables, batch)
     return params(Hq, Hkv, dv, R, window, scale, dqk, bs), batch, rows, Hq, dv, nb
 
 
@@ -309,6 +340,8 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    _shape(out, (rows, Hq, dv), "out")
+    _shape(lse, (rows, Hq), "lse")
     if logit_scale is not None:
         if sink is not None or gate is not None or kv_scales is not None:
             raise ValueError("logit_scale cannot be combined with sink / gate / kv_scales")
@@ -396,6 +429,8 @@ def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, 
     """rba_decode_combine: log-sum-exp merge of the partials in `workspace`
     (rba_decode_combine_gated with sink and/or gate)."""
     p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    _shape(out, (batch * n_q, Hq, dv), "out")
+    _shape(lse, (batch * n_q, Hq), "lse")
     if sink is not None or gate is not None:
         rows = batch * n_q
         _check(lib().rba_decode_combine_gated(
@@ -408,3 +443,4 @@ def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, 
         ctypes.byref(p), batch, n_q, int(num_splits), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.float32, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+

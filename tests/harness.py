@@ -15,9 +15,10 @@ TOL_MEAN = 2e-3    # mean |gpu - oracle|
 
 def oracle_batch(batch: workloads.Batch, rows=None):
     """Float64 oracle on a CPU Batch, one sequence at a time (paging undone by
-    a plain gather of that sequence's blocks). rows: optional global rows; a
-    sampled row at position i is computed as the last query of the sequence's
-    first i+1 keys, which is the same result since later keys are invisible."""
+    a plain gather of that sequence's blocks). rows: optional global rows,
+    computed with the dense row form of the oracle (each sampled row at
+    position i sees keys 0..i of its sequence); without rows every row is
+    computed by the loop form."""
     total = batch.rows
     out = np.full((total, batch.Hq, batch.dv), np.nan)
     lse = np.full((total, batch.Hq), np.nan)
@@ -58,13 +59,20 @@ def oracle_batch(batch: workloads.Batch, rows=None):
             out[start:start + ql] = o
             lse[start:start + ql] = l
         else:
-            for r in local:
-                i = L - ql + r
-                t = start + r
-                o, l = oracle.attend(batch.q[t:t + 1].double().numpy(), k[:i + 1], v[:i + 1],
-                                     rel_rows(t, t + 1), [1], [i + 1], **kw, **gated(t, t + 1))
-                out[t] = o[0]
-                lse[t] = l[0]
+            # sampled rows: the dense row form of the oracle (pinned to the
+            # loop form on the CPU), one matmul per group of rows and head
+            ts = np.asarray([start + r for r in local], dtype=np.int64)
+            g = gated(0, batch.rows)
+            sub = {n: (a[ts] if a is not None else None) for n, a in g.items()}
+            if batch.rel is not None:
+                rel_s = batch.rel[torch.from_numpy(ts)].double().numpy()
+            else:
+                rel_s = oracle.rel_from_proj(batch.r[torch.from_numpy(ts)].double().numpy(),
+                                             batch.proj.double().numpy())
+            o, l = oracle.attend_rows_dense(batch.q[torch.from_numpy(ts)].double().numpy(), k, v, rel_s,
+                                            L - ql + np.asarray(local), **kw, **sub)
+            out[ts] = o
+            lse[ts] = l
         start += ql
     return out, lse
 
@@ -137,3 +145,40 @@ def sample_rows(batch: workloads.Batch, per_edge=16, extra=16, seed=0):
         rows.update((start + rng.integers(0, ql, size=min(extra, ql))).tolist())
         start += ql
     return sorted(rows)
+
+
+def tile_sample_rows(batch: workloads.Batch, edge=256, tile=64, per_tile=2, seed=0):
+    """Rows of a long prefill call to check against the oracle: per sequence
+    the first and last `edge` rows (whole query tiles at both ends), `per_tile`
+    seeded rows from every `tile`-row query tile, and the rows whose position
+    lies within 4 of the extent R or the window W (where the bias or the
+    visible range ends)."""
+    rng = np.random.default_rng(seed)
+    rows, start = set(), 0
+    for b, ql in enumerate(batch.q_lens):
+        L = int(batch.seq_lens[b])
+        ctx = L - ql
+        rows.update(range(start, start + min(edge, ql)))
+        rows.update(range(start + max(0, ql - edge), start + ql))
+        for t0 in range(0, ql, tile):
+            n = min(tile, ql - t0)
+            rows.update((start + t0 + rng.choice(n, size=min(per_tile, n), replace=False)).tolist())
+        for e in (batch.R, batch.W):
+            if e and ctx < e + 4 and e - 4 < L:
+                rows.update(start + p - ctx for p in range(e - 4, e + 4) if ctx <= p < L)
+        start += ql
+    return sorted(rows)
+
+
+def bf16_p_bound(batch: workloads.Batch, rows=None, slack=1e-5):
+    """Per-element bound on |o1 - o2| for two GPU results of the same call
+    that differ only in the reference against which P is rounded to bf16
+    (another split count, another block order). Each result is
+    sum_j p~_j v_j / sum_j p_j with |p~_j - p_j| <= 2^-9 p_j (round to nearest
+    even, 8 significant bits), so it lies within 2^-9 * E_p|v| of the exact
+    value, E_p|v| being the softmax-weighted mean of |v|: the oracle run on
+    |V|. Two results differ by at most 2^-8 * E_p|v|, plus fp32 rounding
+    (`slack`). bf16 caches only."""
+    babs = workloads.Batch(**{**batch.__dict__, "v_cache": batch.v_cache.abs()})
+    ev, _ = oracle_batch(babs, rows)
+    return 2.0 ** -8 * ev + slack

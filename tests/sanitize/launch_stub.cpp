@@ -1,0 +1,52 @@
+// Host-only stand-ins for the kernel launchers, for the sanitizer build of
+// rba_host.cpp (no GPU code is compiled or run). Each one checks the
+// launch arguments the host code prepared against the invariants the
+// kernels rely on and aborts if one is broken, then reports success.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "rba_internal.h"
+
+namespace rba {
+
+static void expect(bool ok, const char* what) {
+    if (!ok) {
+        fprintf(stderr, "launch invariant broken: %s\n", what);
+        abort();
+    }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t) {
+    expect(dv == 64 || dv == 128, "dv");
+    expect(a.q && a.k && a.v && a.cu_q && a.seq_lens && a.tables && a.out, "pointers");
+    expect(a.rel != nullptr || a.r != nullptr, "bias source");
+    expect(a.Hq == a.Hkv * a.G && a.G % a.hpw == 0 && a.n_hc * a.hpw == a.G, "head split");
+    expect(a.QT == 32 * (8 / a.hpw) && a.n_qt >= 1 && a.batch >= 1, "tiles");
+    expect(a.R >= 1 && a.W >= 0 && a.max_blocks >= 1 && a.num_blocks >= 1, "sizes");
+    return hipSuccess;
+}
+
+hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
+    expect(a.r && a.proj && (a.proj_heads == 1 || a.proj_heads == a.Hq), "projection");
+    return launch_prefill(a, dv, s);
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t) {
+    expect(dv == 64 || dv == 128, "dv");
+    expect(a.q && a.k && a.v && a.rel && a.seq_lens && a.tables && a.part_o && a.part_lse, "pointers");
+    expect(a.Hq == a.Hkv * a.G && a.n_cg * 32 >= a.G * a.n_q && a.n_q >= 1, "columns");
+    expect(a.splits >= 1 && a.bps >= 1 && a.batch >= 1, "split plan");
+    // the splits cover the longest visible range
+    const long long nb_max = (a.max_blocks > 0) ? a.max_blocks : 0;
+    expect((long long)a.splits * a.bps >= 1 && nb_max >= 1, "coverage");
+    expect(a.part_lse > a.part_o, "workspace layout");
+    return hipSuccess;
+}
+
+hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t) {
+    expect(dv == 64 || dv == 128, "dv");
+    expect(a.part_o && a.part_lse && a.out && a.pairs >= 1 && a.splits >= 1 && a.splits <= 1024, "combine");
+    return hipSuccess;
+}
+
+}  // namespace rba

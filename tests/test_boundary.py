@@ -64,7 +64,6 @@ def test_validate_prefill_accepts_the_workloads():
     (dict(num_heads_q=30), rba.RBA_ERR_SHAPE),          # not a multiple of Hkv
     (dict(head_dim_v=96), rba.RBA_ERR_UNSUPPORTED),
     (dict(rel_extent=0), rba.RBA_ERR_SHAPE),
-    (dict(rel_extent=510), rba.RBA_ERR_UNSUPPORTED),
     (dict(window=-1), rba.RBA_ERR_SHAPE),
     (dict(scale=math.inf), rba.RBA_ERR_SHAPE),
     (dict(scale=math.nan), rba.RBA_ERR_SHAPE),
@@ -92,7 +91,7 @@ def test_validate_params_head_dim_and_block_size():
     (dict(tab=None), rba.RBA_ERR_NULL),
     (dict(out=None), rba.RBA_ERR_NULL),
     (dict(q=P + 8), rba.RBA_ERR_UNSUPPORTED),          # misaligned
-    (dict(rel=P + 4), rba.RBA_ERR_UNSUPPORTED),
+    (dict(rel=P + 2), rba.RBA_ERR_UNSUPPORTED),        # fp32 rel needs 4-byte alignment
     (dict(nb=0), rba.RBA_ERR_SHAPE),
     (dict(maxb=63), rba.RBA_ERR_SHAPE),                # < ceil(8192/128)
     (dict(batch=-1), rba.RBA_ERR_SHAPE),
@@ -101,6 +100,14 @@ def test_validate_params_head_dim_and_block_size():
 ])
 def test_validate_prefill_rejects_bad_arguments(kw, code):
     assert vprefill(prm(), **kw) == code
+
+
+@pytest.mark.parametrize("R", [1, 5, 127, 510, 1023])
+def test_any_rel_extent_is_accepted(R):
+    """R >= 1 of any size: fp32 rel rows then start at 4-byte multiples,
+    which is all the kernels ask of rel."""
+    assert vprefill(prm(rel_extent=R), rel=P + 4) == rba.RBA_OK
+    assert vdecode(prm(rel_extent=R, window=0), rel=P + 4) == rba.RBA_OK
 
 
 def test_validate_prefill_empty_call_needs_no_pointers():

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from harness import assert_close, errors, oracle_batch, run_decode, run_prefill, sample_rows
+from harness import assert_close, errors, oracle_batch, run_decode, run_prefill, sample_rows, tile_sample_rows
 from relative_position_bias_amd import rba
 
 pytestmark = pytest.mark.gpu
@@ -92,7 +92,10 @@ def test_global_chunked_prefill_logpos_sampled():
         say(f"chunk {c}")
         out, _ = run_prefill(ch)
         torch.cuda.synchronize()
-        rows = sample_rows(ch_cpu, per_edge=8, extra=8, seed=c)
+        # every row of the first and last 256 of the chunk (its first and
+        # last four 64-row query tiles), two seeded rows of every 64-row
+        # tile, and the rows within 4 of position R
+        rows = tile_sample_rows(ch_cpu, seed=c)
         ref, _ = oracle_batch(ch_cpu, rows=rows)
         mx, mean = assert_close(out, ref, rows, f"chunk {c}")
         say(f"  rows {len(rows)} max {mx:.3e} mean {mean:.3e}")

@@ -755,3 +755,109 @@ def test_logpos_mutants_are_caught(kind, monkeypatch):
     with pytest.raises(AssertionError):
         test_logpos_scales_the_bias()
         test_logpos_scales_q_dot_k()
+
+
+# ---------------------------------------------------------------------------
+# un-paging: the gather that turns a block-table cache into contiguous keys
+# ---------------------------------------------------------------------------
+def _paged_case(seed=17, Hk=3, d=5, bs=8):
+    """Two sequences (one ending inside its last block) in a pool of blocks
+    placed by a seeded permutation, plus a spare block that no table uses."""
+    rng = np.random.default_rng(seed)
+    seq_lens = [19, 8]
+    nbs = [(L + bs - 1) // bs for L in seq_lens]
+    perm = rng.permutation(sum(nbs) + 1)
+    tables, o = [], 0
+    for nb in nbs:
+        tables.append([int(x) for x in perm[o:o + nb]] + [-1])   # a trailing unused entry
+        o += nb
+    cache = rng.standard_normal((sum(nbs) + 1, Hk, bs, d))
+    return cache, tables, seq_lens, bs
+
+
+def _per_token_gather(cache, tables, seq_lens, bs):
+    """Position j of sequence b is slot j % bs of the block in table entry
+    j // bs ("Inkling-Small on Gaudi 2", "Attention with a relative bias":
+    key positions are block ordinal x block size + slot), one token at a time."""
+    rows = []
+    for b, L in enumerate(seq_lens):
+        for j in range(L):
+            rows.append(cache[tables[b][j // bs], :, j % bs, :])
+    return np.stack(rows)
+
+
+def test_unpage_matches_per_token_gather():
+    cache, tables, seq_lens, bs = _paged_case()
+    got = oracle.unpage(cache, tables, seq_lens, block_size=bs)
+    want = _per_token_gather(cache, tables, seq_lens, bs)
+    assert got.shape == (sum(seq_lens), cache.shape[1], cache.shape[3])
+    np.testing.assert_array_equal(got, want)
+
+
+def _unpage_mutant(kind):
+    def f(cache, block_tables, seq_lens, block_size=128):
+        cache = np.asarray(cache)
+        parts = []
+        for b, L in enumerate(seq_lens):
+            nb = (int(L) + block_size - 1) // block_size
+            idx = np.asarray(block_tables[b][:nb], dtype=np.int64)
+            if kind == "reversed_table":
+                idx = idx[::-1]
+            blocks = cache[idx]
+            if kind == "no_transpose":   # [nb, H, bs, d] reshaped as if it were [nb, bs, H, d]
+                seq = blocks.reshape(nb * block_size, cache.shape[1], cache.shape[3])
+            else:
+                seq = blocks.transpose(0, 2, 1, 3).reshape(nb * block_size, cache.shape[1], cache.shape[3])
+            if kind == "first_slots_dropped":
+                seq = seq[1:]
+                parts.append(seq[:int(L) - 1])
+                continue
+            parts.append(seq[:int(L)])
+        return np.concatenate(parts, axis=0)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_transpose", "reversed_table", "first_slots_dropped"])
+def test_unpage_mutants_are_caught(kind):
+    cache, tables, seq_lens, bs = _paged_case()
+    want = _per_token_gather(cache, tables, seq_lens, bs)
+    got = _unpage_mutant(kind)(cache, tables, seq_lens, block_size=bs)
+    assert got.shape != want.shape or not np.array_equal(got, want), kind
+
+
+# ---------------------------------------------------------------------------
+# the dense row form of the oracle (used for many sampled rows of long inputs)
+# ---------------------------------------------------------------------------
+DENSE_GRID = [
+    # seq_len, positions, Hq, Hkv, dqk, dv, R, W
+    (40, [0, 1, 5, 39, 20, 33], 4, 1, 16, 8, 9, 0),
+    (70, [69, 3, 64, 12], 6, 2, 8, 16, 64, 20),
+    (33, list(range(33)), 4, 4, 8, 8, 1, 1),
+    (90, [10, 89, 45, 50, 51, 88], 8, 2, 16, 16, 7, 33),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_GRID)
+@pytest.mark.parametrize("extras", ["plain", "gated", "logpos"])
+def test_dense_rows_match_the_loop_oracle(case, extras):
+    """attend_rows_dense equals attend (the loop form, pinned by everything
+    above) on the same rows, to float64 rounding."""
+    L, pos, Hq, Hkv, dqk, dv, R, W = case
+    rng = np.random.default_rng(L + R + W)
+    k = rng.standard_normal((L, Hkv, dqk))
+    v = rng.standard_normal((L, Hkv, dv))
+    qa = rng.standard_normal((L, Hq, dqk))
+    rela = 0.5 * rng.standard_normal((L, Hq, R))
+    kw = {}
+    if extras == "gated":
+        kw = dict(sink=2 * rng.standard_normal((L, Hq)), gate=2 * rng.standard_normal((L, Hq)))
+    if extras == "logpos":
+        kw = dict(logit_scale=1.0 + 0.25 * rng.random(L))
+    scale = 1.0 / math.sqrt(dqk)
+    full, lfull = oracle.attend(qa, k, v, rela, [L], [L], rel_extent=R, window=W, scale=scale, **kw)
+    p = np.asarray(pos)
+    sub = {n: (a[p] if a is not None else None) for n, a in kw.items()}
+    o, l = oracle.attend_rows_dense(qa[p], k, v, rela[p], p, rel_extent=R, window=W, scale=scale,
+                                    group=4, **sub)
+    np.testing.assert_allclose(o, full[p], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lfull[p], rtol=0, atol=1e-12)
