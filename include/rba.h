@@ -365,6 +365,30 @@ int rba_decode_split_fp8(const rba_attn_params* params,
                          int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rba_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The split partials go to a scratch array that the
+ * library's code object holds on each GPU (RBA_NOALLOC_SCRATCH_BYTES bytes per
+ * GPU, kept until the process ends); the call allocates nothing and calls no
+ * allocating routine. Its contents on entry are ignored (every partial is
+ * written before it is read), so nothing needs clearing between calls; but
+ * every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (several streams or threads at once) race and give wrong results.
+ * Arguments, results and errors are as rba_decode (same kernels, same split
+ * plan); RBA_ERR_WORKSPACE if the call needs more than
+ * RBA_NOALLOC_SCRATCH_BYTES (see rba_decode_workspace_size), RBA_ERR_HIP if
+ * the scratch address cannot be taken on the current device.
+ */
+#define RBA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int rba_decode_noalloc(const rba_attn_params* params,
+                       const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                       const float* rel, const int32_t* seq_lens,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                       float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

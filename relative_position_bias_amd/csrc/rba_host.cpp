@@ -527,6 +527,34 @@ int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache
     return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
 }
 
+int rba_decode_noalloc(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                       int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                       int32_t num_splits, float* out, float* lse, void* stream) {
+    // Validate against the scratch's size first (no HIP call), then take its
+    // device address on the current device.
+    alignas(256) static char placeholder;
+    bool nothing;
+    int32_t splits = 0;
+    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, &placeholder,
+                             (size_t)-1, out, lse, true, &splits, &nothing);
+    if (rc || nothing) return rc;
+    const size_t need = ws_bytes(params, batch, n_q, splits);
+    if (need > RBA_NOALLOC_SCRATCH_BYTES)
+        return fail(RBA_ERR_WORKSPACE, "the call needs %zu bytes of scratch; rba_decode_noalloc holds %zu "
+                    "(use rba_decode with a workspace)", need, (size_t)RBA_NOALLOC_SCRATCH_BYTES);
+    void* scratch = nullptr;
+    hipError_t e = rba::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, scratch);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = rba::launch_decode_split(a, params->head_dim_v, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    return rba_decode_combine(params, batch, n_q, splits, scratch, need, out, lse, stream);
+}
+
 int rba_decode_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
                      int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,

@@ -70,4 +70,10 @@ hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s);
 
+// The device scratch of rba_decode_noalloc: a file-scope device array of
+// RBA_NOALLOC_SCRATCH_BYTES bytes in the kernels' code object, one copy per
+// GPU. Its device address on the current device (looked up once per device
+// with hipGetSymbolAddress, with that device current) is returned in *ptr.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace rba

@@ -66,6 +66,9 @@
 
 #include <type_traits>
 
+#include <atomic>
+
+#include "rba.h"
 #include "rba_internal.h"
 
 namespace rba {
@@ -1904,6 +1907,30 @@ hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
         else hipLaunchKernelGGL((decode_split_kernel<64, false>), g, blk, 0, s, a);
     }
     return hipGetLastError();
+}
+
+// Scratch of rba_decode_noalloc (for callers that cannot allocate): the
+// split partials live here instead of in a caller's workspace. Each GPU holds
+// its own copy from the first launch until the process ends. In host code the
+// name is only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __attribute__((aligned(256))) char scratch[RBA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s) {

@@ -86,7 +86,11 @@ _SIGNATURES = {
     "rba_decode_split_fp8": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, ctypes.c_float,
                                             ctypes.c_float, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
                                             _ptr, _size, _ptr]),
+    "rba_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                          _i32, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr]),
 }
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # RBA_NOALLOC_SCRATCH_BYTES in include/rba.h
 
 _lib = None
 
@@ -444,3 +448,27 @@ def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, 
         workspace.numel(), _dev(out, torch.float32, "out"),
         _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
 
+
+def decode_noalloc(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
+                   max_seq_len: int, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rba_decode_noalloc: rba_decode with the split partials in the
+    library's own device scratch (no workspace argument; the library
+    allocates nothing). Calls that overlap on one GPU share that scratch and
+    race. bf16 caches; out / lse are allocated with torch if not given."""
+    p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
+                                                window, scale)
+    if out is None:
+        out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    _shape(out, (rows, Hq, dv), "out")
+    _shape(lse, (rows, Hq), "lse")
+    _check(lib().rba_decode_noalloc(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits), _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+    return out, lse

@@ -50,3 +50,14 @@ hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t) {
 }
 
 }  // namespace rba
+
+namespace rba {
+
+// No GPU: the scratch address of the no-allocation decode is a fake,
+// 256-byte aligned host value that the stand-in launchers never dereference.
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = reinterpret_cast<void*>(0x7f0000000000ull);
+    return hipSuccess;
+}
+
+}  // namespace rba
