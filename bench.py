@@ -1,13 +1,20 @@
 """Benchmark of the relative-bias attention hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-  * rba_prefill on the Inkling-Small local-layer prefill (one 8,192-token
-    sequence, 32 query / 8 KV heads, head size 128, window 512, rel extent
-    512, paged in permuted 128-token blocks), then
-  * rba_decode on the global-layer paged decode (16 sequences with seeded
-    lengths uniform in [8K, 128K], one query token each, 32/8 heads, rel
-    extent 1024, block size 128; every sequence on its own blocks, so no block
-    is read twice) as its two stages, split-KV then log-sum-exp combine.
+One step = one pass of the whole path over one batch of synthetic input, one
+call sequence per workload the path is quoted on:
+  * local_prefill: rba_prefill on the Inkling-Small local-layer prefill (one
+    8,192-token sequence, 32 query / 8 KV heads, head size 128, window 512,
+    rel extent 512, paged in permuted 128-token blocks);
+  * global_prefill: the global-layer chunked prefill, a 32,768-token
+    sequence as 4 rba_prefill calls of 8,192 rows each over all cached keys
+    before them (no window, rel extent 1024);
+  * decode: rba_decode on the global-layer paged decode (16 sequences with
+    seeded lengths uniform in [8K, 128K], one query token each, 32/8 heads,
+    rel extent 1024; every sequence on its own blocks, so no block is read
+    twice) as its two stages, split-KV then log-sum-exp combine;
+  * verify_b1, verify_b8: rba_decode on the diff-headdim verify (100,000-token
+    context, 4 query tokens per sequence, 64/8 heads, value head 64, rel
+    extent 1024) at batch 1 and batch 8, again as split + combine.
 Inputs are resident in HBM before timing. Each call is timed with HIP events
 on the stream it is launched on, and the whole step with host clocks around
 synchronisations.
@@ -15,9 +22,10 @@ synchronisations.
 value = whole-step fraction of the MI355X roofline, in percent:
   100 * sum_calls max(F/peak_mfma, B/peak_hbm) / sum_calls measured time
 with F, B the algorithmic flops / bytes (visible (query, key) pairs only; K/V,
-q, rel, out and tables read or written once). Per-call TFLOP/s and GB/s are
-reported beside it, plus the roofline of the dominant kernel and the float64
-CPU oracle timed on a bounded sample of the same workload.
+q, rel, out and tables read or written once). Per-leg TFLOP/s, GB/s and roof
+fractions are reported beside it, plus the roofline of the dominant kernel
+(and of the decode split kernel) and the float64 CPU oracle timed on a
+bounded sample of the same workloads.
 """
 from __future__ import annotations
 
@@ -35,12 +43,21 @@ for _p in (ROOT, os.path.join(ROOT, "tests")):
 METRIC = "rel-bias attn prefill TFLOP/s + decode HBM GB/s, % of MI355X roofline"
 PEAK_MFMA_BF16 = 2516.6e12   # dense bf16 MFMA, FLOP/s (256 CU x 2.4 GHz x 4096)
 PEAK_HBM = 8.0e12            # HBM3E, B/s
-PREFILL = "local_prefill_8k"
-DECODE = "paged_decode_16x8k_128k_disjoint"
 DQK = 128
+# (leg, workload) of one step
+LEGS = [
+    ("local_prefill", "local_prefill_8k"),
+    ("global_prefill", "global_chunked_prefill_32k"),
+    ("decode", "paged_decode_16x8k_128k_disjoint"),
+    ("verify_b1", "verify_decode_b1_100k"),
+    ("verify_b8", "verify_decode_b8_100k"),
+]
 
-
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode16_split_kernel_paged_decode_16_disjoint_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILES = {
+    "decode": os.path.join(PROFILES, "decode16_split_kernel_paged_decode_16_disjoint_traffic.txt"),
+    "global_prefill": os.path.join(PROFILES, "prefill_kernel_global_chunked_prefill_32k_traffic.txt"),
+}
 CSRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc")
 KERNEL_SRCS = [os.path.join(CSRC, "rba_kernels.hip"), os.path.join(CSRC, "rba_internal.h")]
 HOST_SRCS = [os.path.join(CSRC, "rba_host.cpp")]
@@ -62,15 +79,16 @@ def code_digest(paths):
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode split kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel code
-    or the host code (which sets the launch, e.g. the split count) has changed
-    since those counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(leg):
+    """HBM bytes per launch of a leg's dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none or
+    the kernel code or the host code (which sets the launch, e.g. the split
+    count) has changed since those counters were taken."""
+    path = TRAFFIC_FILES.get(leg)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -121,54 +139,21 @@ def roof_time(flops, nbytes):
     return max(flops / PEAK_MFMA_BF16, nbytes / PEAK_HBM)
 
 
-def _first_sequences(b, m):
+def _sequence(b, m):
+    """Sequence m of a decode Batch as a Batch of its own (CPU)."""
     import workloads as W
     sub = W.Batch(**{**b.__dict__})
-    sub.q = b.q[:m * b.n_q]
-    sub.rel = b.rel[:m * b.n_q]
-    sub.seq_lens = b.seq_lens[:m]
-    sub.block_tables = b.block_tables[:m]
-    sub.q_lens = b.q_lens[:m]
+    sub.q = b.q[m * b.n_q:(m + 1) * b.n_q]
+    sub.rel = b.rel[m * b.n_q:(m + 1) * b.n_q]
+    sub.seq_lens = b.seq_lens[m:m + 1]
+    sub.block_tables = b.block_tables[m:m + 1]
+    sub.q_lens = b.q_lens[m:m + 1]
     return sub
 
 
-def cpu_baseline(pre_cpu, dec_cpu, budget_s):
-    """The float64 oracle (as it stands) on a bounded sample of the step:
-    prefill query rows 0..1023 (all heads), then decode sequences one at a
-    time until about `budget_s` seconds of CPU work in total."""
-    from harness import oracle_batch
-
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    rows = list(range(0, 1024))
-    t0 = time.perf_counter()
-    oracle_batch(pre_cpu, rows=rows)
-    t_pre = time.perf_counter() - t0
-    t_dec, m = 0.0, 0
-    while m < len(dec_cpu.q_lens) and (m == 0 or t_pre + t_dec < budget_s):
-        one = _first_sequences(dec_cpu, m + 1)
-        one.q, one.rel = one.q[m * one.n_q:], one.rel[m * one.n_q:]
-        one.seq_lens, one.block_tables, one.q_lens = one.seq_lens[m:], one.block_tables[m:], one.q_lens[m:]
-        t0 = time.perf_counter()
-        oracle_batch(one)
-        t_dec += time.perf_counter() - t0
-        m += 1
-    f_pre, b_pre = _sampled_prefill_work(pre_cpu, rows)
-    f_dec, b_dec, _ = algorithmic(_first_sequences(dec_cpu, m), "decode")
-    t_roof = roof_time(f_pre, b_pre) + roof_time(f_dec, b_dec)
-    t_cpu = t_pre + t_dec
-    return {
-        "value": round(100.0 * t_roof / t_cpu, 6),
-        "unit": "% of MI355X roofline",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"prefill rows 0-{len(rows) - 1} of {pre_cpu.rows} (all {pre_cpu.Hq} heads) + "
-                   f"decode sequences 0-{m - 1} of {len(dec_cpu.q_lens)}; float64 C oracle, OpenMP"),
-        "seconds": round(t_cpu, 3),
-        "gflops": round((f_pre + f_dec) / t_cpu / 1e9, 3),
-    }
-
-
 def _sampled_prefill_work(b, rows):
+    """Algorithmic (flops, bytes) of the given contiguous rows of a
+    one-sequence prefill Batch."""
     L = int(b.seq_lens[0])
     ctx = L - b.q_lens[0]
     pairs = biased = 0
@@ -183,6 +168,65 @@ def _sampled_prefill_work(b, rows):
     nbytes = (len(rows) * b.Hq * DQK * 2 + keys * b.Hkv * (DQK + b.dv) * 2 + biased * b.Hq * 4
               + len(rows) * b.Hq * b.dv * 4)
     return flops, nbytes
+
+
+def cpu_baseline(inputs, budget_s):
+    """The float64 oracle (its loop form, as it stands) on a bounded sample of
+    every leg of the step: local prefill rows 0-255 and 4096-4351, the last 2
+    rows of the last global-prefill chunk (its most expensive rows), the
+    batch-1 verify call whole, then decode sequences one at a time until about
+    `budget_s` seconds of CPU work in total. Reported as the fraction of the
+    MI355X roofline the oracle reaches on that sample."""
+    from harness import oracle_batch
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t_cpu = t_roof = flops = 0.0
+    parts = []
+
+    def timed(batch, rows=None):
+        t0 = time.perf_counter()
+        oracle_batch(batch, rows=rows, form="loop")
+        return time.perf_counter() - t0
+
+    pre = inputs["local_prefill"][0][0]
+    for seg in (range(0, 256), range(4096, 4352)):
+        t_cpu += timed(pre, list(seg))
+        f, nb = _sampled_prefill_work(pre, list(seg))
+        t_roof += roof_time(f, nb)
+        flops += f
+    parts.append("local prefill rows 0-255 and 4096-4351 (all heads)")
+    ch = inputs["global_prefill"][-1][0]
+    rows = [ch.rows - 2, ch.rows - 1]
+    t_cpu += timed(ch, rows)
+    f, nb = _sampled_prefill_work(ch, rows)
+    t_roof += roof_time(f, nb)
+    flops += f
+    parts.append(f"global prefill chunk {len(inputs['global_prefill']) - 1} rows {rows[0]}-{rows[1]}")
+    vb1 = inputs["verify_b1"][0][0]
+    t_cpu += timed(vb1)
+    f, nb, _ = algorithmic(vb1, "decode")
+    t_roof += roof_time(f, nb)
+    flops += f
+    parts.append("verify B=1 whole call")
+    dec = inputs["decode"][0][0]
+    m = 0
+    while m < len(dec.q_lens) and (m == 0 or t_cpu < budget_s):
+        one = _sequence(dec, m)
+        t_cpu += timed(one)
+        f, nb, _ = algorithmic(one, "decode")
+        t_roof += roof_time(f, nb)
+        flops += f
+        m += 1
+    parts.append(f"decode sequences 0-{m - 1} of {len(dec.q_lens)}")
+    return {
+        "value": round(100.0 * t_roof / t_cpu, 6),
+        "unit": "% of MI355X roofline",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "; ".join(parts) + "; float64 C oracle (loop form), OpenMP",
+        "seconds": round(t_cpu, 3),
+        "gflops": round(flops / t_cpu / 1e9, 3),
+    }
 
 
 def workload_report(name, steps, warmup, dev, flush=True):
@@ -265,37 +309,58 @@ def main():
     if args.workload:
         workload_report(args.workload, args.steps, args.warmup, dev, flush=not args.no_flush)
         return
-    t_gen = time.perf_counter()
-    pre_cpu = W.build(PREFILL)
-    dec_cpu = W.build(DECODE)
-    pre = pre_cpu.to(dev)
-    dec = dec_cpu.to(dev)
-    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
-
-    splits = rba.plan_splits(dec.Hq, dec.Hkv, dec.dv, dec.R, dec.W, dec.scale, len(dec.q_lens), dec.n_q,
-                             dec.max_seq_len, torch.cuda.get_device_properties(dev).multi_processor_count)
-    ws = torch.empty(rba.workspace_size(dec.Hq, dec.Hkv, dec.dv, dec.R, dec.W, dec.scale, len(dec.q_lens),
-                                        dec.n_q, dec.max_seq_len, splits), dtype=torch.uint8, device=dev)
-    pre_out = torch.empty((pre.rows, pre.Hq, pre.dv), dtype=torch.float32, device=dev)
-    dec_out = torch.empty((dec.rows, dec.Hq, dec.dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
-    def prefill_call():
-        rba.prefill(pre.q, pre.k_cache, pre.v_cache, pre.rel, pre.cu_q, pre.seq_lens, pre.block_tables,
-                    window=pre.W, scale=pre.scale, max_q_len=pre.max_q_len, max_seq_len=pre.max_seq_len,
-                    out=pre_out, stream=stream)
+    # inputs of every leg, on the CPU (for the algorithmic counts and the
+    # oracle sample) and on the GPU; a leg is a list of (cpu, gpu) calls
+    t_gen = time.perf_counter()
+    inputs = {}
+    for leg, name in LEGS:
+        full = W.build(name)
+        gpu = full.to(dev)
+        if W.WORKLOADS[name]["kind"] == "chunked":
+            inputs[leg] = list(zip(W.chunks(name, full), W.chunks(name, gpu)))
+        else:
+            inputs[leg] = [(full, gpu)]
+        print(f"[bench] {leg}: {name} ready ({time.perf_counter() - t_gen:.1f}s)", file=sys.stderr, flush=True)
 
-    def split_call():
-        rba.decode_split(dec.q, dec.k_cache, dec.v_cache, dec.rel, dec.seq_lens, dec.block_tables,
-                         n_q=dec.n_q, window=dec.W, scale=dec.scale, max_seq_len=dec.max_seq_len,
-                         num_splits=splits, workspace=ws, stream=stream)
+    # the calls of one step, in order: (leg, call name, fn, flops, bytes)
+    calls = []
+    splits_of = {}
+    for leg, _ in LEGS:
+        for c, (b_cpu, b) in enumerate(inputs[leg]):
+            f, nbytes, read = algorithmic(b_cpu, b.kind)
+            if b.kind == "prefill":
+                out = torch.empty((b.rows, b.Hq, b.dv), dtype=torch.float32, device=dev)
 
-    def combine_call():
-        rba.decode_combine(Hq=dec.Hq, Hkv=dec.Hkv, dv=dec.dv, rel_extent=dec.R, window=dec.W,
-                           scale=dec.scale, batch=len(dec.q_lens), n_q=dec.n_q, num_splits=splits,
-                           workspace=ws, out=dec_out, stream=stream)
+                def prefill_call(b=b, out=out):
+                    rba.prefill(b.q, b.k_cache, b.v_cache, b.rel, b.cu_q, b.seq_lens, b.block_tables,
+                                window=b.W, scale=b.scale, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
+                                out=out, stream=stream)
+                calls.append((leg, f"prefill{c}", prefill_call, f, nbytes))
+                continue
+            batch = len(b.q_lens)
+            splits = rba.plan_splits(b.Hq, b.Hkv, b.dv, b.R, b.W, b.scale, batch, b.n_q, b.max_seq_len, n_cus)
+            splits_of[leg] = splits
+            ws = torch.empty(rba.workspace_size(b.Hq, b.Hkv, b.dv, b.R, b.W, b.scale, batch, b.n_q,
+                                                b.max_seq_len, splits), dtype=torch.uint8, device=dev)
+            out = torch.empty((b.rows, b.Hq, b.dv), dtype=torch.float32, device=dev)
 
-    calls = [("prefill", prefill_call), ("decode_split", split_call), ("decode_combine", combine_call)]
+            def split_call(b=b, ws=ws, splits=splits):
+                rba.decode_split(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
+                                 window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=splits,
+                                 workspace=ws, stream=stream)
+
+            def combine_call(b=b, ws=ws, splits=splits, out=out, batch=batch):
+                rba.decode_combine(Hq=b.Hq, Hkv=b.Hkv, dv=b.dv, rel_extent=b.R, window=b.W, scale=b.scale,
+                                   batch=batch, n_q=b.n_q, num_splits=splits, workspace=ws, out=out,
+                                   stream=stream)
+            # the split kernel reads the inputs; the combine writes out (the
+            # workspace traffic is not algorithmic)
+            calls.append((leg, "split", split_call, f, read))
+            calls.append((leg, "combine", combine_call, 0, nbytes - read))
+
     if args.copy_probe_mib > 0:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -304,50 +369,86 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        for _, fn in calls:
+        for _, _, fn, _, _ in calls:
             fn()
     torch.cuda.synchronize()
 
-    events = {name: [] for name, _ in calls}
+    events = [[] for _ in calls]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for name, fn in calls:
+        for k, (_, _, fn, _, _) in enumerate(calls):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
             e1.record(stream)
-            events[name].append((e0, e1))
+            events[k].append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {name: sum(a.elapsed_time(b) for a, b in ev) / len(ev) for name, ev in events.items()}
+    ms = [sum(a.elapsed_time(b) for a, b in ev) / len(ev) for ev in events]
     ms_per_step = 1e3 * wall / args.steps
 
-    f_pre, b_pre, _ = algorithmic(pre_cpu, "prefill")
-    f_dec, b_dec, b_split = algorithmic(dec_cpu, "decode")
-    t_pre = ms["prefill"] / 1e3
-    t_split = ms["decode_split"] / 1e3
-    t_dec = (ms["decode_split"] + ms["decode_combine"]) / 1e3
-    roof_pre, roof_dec = roof_time(f_pre, b_pre), roof_time(f_dec, b_dec)
-    value = 100.0 * (roof_pre + roof_dec) / (t_pre + t_dec)
+    # per leg: time, rates, roof fractions; roofline-weighted step value
+    legs = {}
+    roof_sum = t_sum = 0.0
+    for leg, name in LEGS:
+        ks = [k for k, c in enumerate(calls) if c[0] == leg]
+        t = sum(ms[k] for k in ks) / 1e3
+        f = sum(calls[k][3] for k in ks)
+        nb = sum(calls[k][4] for k in ks)
+        # roof per call: each prefill chunk is its own call; a decode is one call (split + combine)
+        if calls[ks[0]][1].startswith("prefill"):
+            roof = sum(roof_time(calls[k][3], calls[k][4]) for k in ks)
+        else:
+            roof = roof_time(f, nb)
+        roof_sum += roof
+        t_sum += t
+        legs[leg] = {"workload": name, "ms": round(t * 1e3, 4), "tflops": round(f / t / 1e12, 2),
+                     "gbps": round(nb / t / 1e9, 1), "frac_mfma": round(f / t / PEAK_MFMA_BF16, 4),
+                     "frac_hbm": round(nb / t / PEAK_HBM, 4), "frac_roof": round(roof / t, 4),
+                     "flops": f, "bytes": nb}
+        if len(ks) > 1 and calls[ks[0]][1].startswith("prefill"):
+            legs[leg]["chunk_ms"] = [round(ms[k], 4) for k in ks]
+        if leg in splits_of:
+            legs[leg].update(split_ms=round(ms[ks[0]], 4), combine_ms=round(ms[ks[1]], 4), splits=splits_of[leg])
+    value = 100.0 * roof_sum / t_sum
 
-    # dominant kernel: the one with the larger share of the step
-    if t_split >= t_pre:
-        achieved = b_split / t_split / 1e9
-        # G * n_q <= 16 runs the 16-column split kernel
-        kname = "decode16_split_kernel<128, false>" if dec.Hq // dec.Hkv * dec.n_q <= 16 else "decode_split_kernel<128, false>"
-        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                    "traffic": measured_traffic(), "algorithmic_bytes_per_launch": b_split,
-                    "avg_launch_ms": round(ms["decode_split"], 4)}
-    else:
-        achieved = b_pre / t_pre / 1e9
-        pname = "prefill_kernel<128, true>" if pre.W > 0 else "prefill_kernel<128, false>"
-        roofline = {"kernel": pname, "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
-                    "traffic": None, "algorithmic_bytes_per_launch": b_pre,
-                    "avg_launch_ms": round(ms["prefill"], 4)}
+    def prefill_roofline(leg):
+        ks = [k for k, c in enumerate(calls) if c[0] == leg]
+        b = inputs[leg][0][1]
+        t = sum(ms[k] for k in ks) / 1e3
+        f = sum(calls[k][3] for k in ks)
+        nb = sum(calls[k][4] for k in ks)
+        kname = f"prefill_kernel<{b.dv}, {'true' if b.W > 0 else 'false'}>"
+        if f / PEAK_MFMA_BF16 >= nb / PEAK_HBM:
+            achieved = f / t / 1e12
+            blk = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
+                   "peak": PEAK_MFMA_BF16 / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (PEAK_MFMA_BF16 / 1e12), 4)}
+        else:
+            achieved = nb / t / 1e9
+            blk = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                   "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
+        blk.update(traffic=measured_traffic(leg), launches=len(ks),
+                   algorithmic_flops_per_launch=f // len(ks), algorithmic_bytes_per_launch=nb // len(ks),
+                   avg_launch_ms=round(t * 1e3 / len(ks), 4))
+        return blk
+
+    def decode_roofline(leg):
+        ks = [k for k, c in enumerate(calls) if c[0] == leg]
+        b = inputs[leg][0][1]
+        t = ms[ks[0]] / 1e3
+        nb = calls[ks[0]][4]
+        achieved = nb / t / 1e9
+        cols = b.Hq // b.Hkv * b.n_q
+        kname = (f"decode16_split_kernel<{b.dv}, false>" if cols <= 16 else f"decode_split_kernel<{b.dv}, false>")
+        return {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": measured_traffic(leg),
+                "algorithmic_bytes_per_launch": nb, "avg_launch_ms": round(ms[ks[0]], 4)}
+
+    # dominant kernel: the leg with the largest share of the step
+    dom = max(legs, key=lambda leg: legs[leg]["ms"])
+    roofline = prefill_roofline(dom) if "prefill" in dom else decode_roofline(dom)
 
     line = {
         "metric": METRIC,
@@ -363,25 +464,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{PREFILL} + {DECODE}",
-            "prefill": {"seq_len": pre.max_seq_len, "Hq": pre.Hq, "Hkv": pre.Hkv, "head_dim": DQK,
-                        "dv": pre.dv, "window": pre.W, "rel_extent": pre.R, "block_size": 128},
-            "decode": {"batch": len(dec.q_lens), "n_q": dec.n_q, "seq_lens_sum": int(sum(dec_cpu.seq_lens.tolist())),
-                       "Hq": dec.Hq, "Hkv": dec.Hkv, "dv": dec.dv, "rel_extent": dec.R, "splits": splits,
-                       "block_size": 128},
+            "workload": " + ".join(name for _, name in LEGS),
+            "local_prefill": {"seq_len": 8192, "Hq": 32, "Hkv": 8, "head_dim": DQK, "dv": 128, "window": 512,
+                              "rel_extent": 512, "block_size": 128},
+            "global_prefill": {"seq_len": 32768, "chunks": 4, "chunk": 8192, "Hq": 32, "Hkv": 8, "head_dim": DQK,
+                               "dv": 128, "window": 0, "rel_extent": 1024, "block_size": 128},
+            "decode": {"batch": 16, "n_q": 1, "seq_lens_sum": int(sum(inputs["decode"][0][0].seq_lens.tolist())),
+                       "Hq": 32, "Hkv": 8, "dv": 128, "rel_extent": 1024, "block_size": 128},
+            "verify": {"batch": [1, 8], "n_q": 4, "seq_len": 100000, "Hq": 64, "Hkv": 8, "dv": 64,
+                       "rel_extent": 1024, "block_size": 128},
         },
-        "prefill": {"ms": round(ms["prefill"], 4), "tflops": round(f_pre / t_pre / 1e12, 2),
-                    "gbps": round(b_pre / t_pre / 1e9, 1), "frac_mfma": round(f_pre / t_pre / PEAK_MFMA_BF16, 4),
-                    "frac_hbm": round(b_pre / t_pre / PEAK_HBM, 4), "flops": f_pre, "bytes": b_pre},
-        "decode": {"ms": round(t_dec * 1e3, 4), "split_ms": round(ms["decode_split"], 4),
-                   "combine_ms": round(ms["decode_combine"], 4), "gbps": round(b_dec / t_dec / 1e9, 1),
-                   "frac_hbm": round(b_dec / t_dec / PEAK_HBM, 4), "flops": f_dec, "bytes": b_dec},
+        **legs,
         "roofline": roofline,
+        "roofline_decode": decode_roofline("decode"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(pre_cpu, dec_cpu, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

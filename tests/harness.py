@@ -13,12 +13,13 @@ TOL_MAX = 1.5e-2   # max |gpu - oracle| over every compared element
 TOL_MEAN = 2e-3    # mean |gpu - oracle|
 
 
-def oracle_batch(batch: workloads.Batch, rows=None):
+def oracle_batch(batch: workloads.Batch, rows=None, form="dense"):
     """Float64 oracle on a CPU Batch, one sequence at a time (paging undone by
     a plain gather of that sequence's blocks). rows: optional global rows,
-    computed with the dense row form of the oracle (each sampled row at
-    position i sees keys 0..i of its sequence); without rows every row is
-    computed by the loop form."""
+    computed with the dense row form of the oracle (form="dense"; each
+    sampled row at position i sees keys 0..i of its sequence) or one row at a
+    time by the loop form (form="loop"); without rows every row is computed by
+    the loop form."""
     total = batch.rows
     out = np.full((total, batch.Hq, batch.dv), np.nan)
     lse = np.full((total, batch.Hq), np.nan)
@@ -58,6 +59,14 @@ def oracle_batch(batch: workloads.Batch, rows=None):
                                  **gated(start, start + ql))
             out[start:start + ql] = o
             lse[start:start + ql] = l
+        elif form == "loop":
+            for r in local:
+                i = L - ql + r
+                t = start + r
+                o, l = oracle.attend(batch.q[t:t + 1].double().numpy(), k[:i + 1], v[:i + 1],
+                                     rel_rows(t, t + 1), [1], [i + 1], **kw, **gated(t, t + 1))
+                out[t] = o[0]
+                lse[t] = l[0]
         else:
             # sampled rows: the dense row form of the oracle (pinned to the
             # loop form on the CPU), one matmul per group of rows and head
