@@ -229,13 +229,28 @@ def cpu_baseline(inputs, budget_s):
     }
 
 
-def workload_report(name, steps, warmup, dev, flush=True):
+def copy_probe(mib, dev):
+    """One plain device-to-device copy of `mib` MiB (torch copy_), used to
+    calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters in the same run."""
+    import torch
+
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def workload_report(name, steps, warmup, dev, flush=True, copy_mib=0):
     """Per-call times of one named workload (each call timed with events on
     its stream), with algorithmic TFLOP/s, GB/s and roofline fractions."""
     import torch
 
     import workloads as W
     from harness import run_decode, run_prefill
+
+    if copy_mib > 0:
+        copy_probe(copy_mib, dev)
 
     full = W.build(name)
     gpu = full.to(dev)
@@ -307,7 +322,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload:
-        workload_report(args.workload, args.steps, args.warmup, dev, flush=not args.no_flush)
+        workload_report(args.workload, args.steps, args.warmup, dev, flush=not args.no_flush,
+                        copy_mib=args.copy_probe_mib)
         return
     stream = torch.cuda.current_stream()
     n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -362,11 +378,7 @@ def main():
             calls.append((leg, "combine", combine_call, 0, nbytes - read))
 
     if args.copy_probe_mib > 0:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(args.copy_probe_mib, dev)
 
     for _ in range(args.warmup):
         for _, _, fn, _, _ in calls:
