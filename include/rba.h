@@ -179,7 +179,8 @@ int rba_prefill_relproj(const rba_attn_params* params,
  *   logit_scale  device fp32, [total_q] for rba_prefill_logpos (row t of q)
  *                and [batch * n_q] for rba_decode_logpos; finite values
  *   all other arguments as rba_prefill / rba_decode (bf16 K/V; no sink or
- *   gate). Errors: as rba_prefill / rba_decode; RBA_ERR_NULL if logit_scale
+ *   gate: rba_prefill_ex / rba_decode_ex combine them). Errors: as
+ *   rba_prefill / rba_decode; RBA_ERR_NULL if logit_scale
  *   is NULL for a non-empty call, RBA_ERR_UNSUPPORTED if it is not 4-byte
  *   aligned.
  */
@@ -364,6 +365,69 @@ int rba_decode_split_fp8(const rba_attn_params* params,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Any combination of the optional terms above in one call: the gated output
+ * (sink, gate; rba_prefill_gated / rba_decode_gated), the per-row logit scale
+ * (rba_prefill_logpos / rba_decode_logpos) and, for the decode, the e4m3 K/V
+ * cache (rba_decode_fp8). Sources: those entry points' sections above. The
+ * terms act at different places, so their composition is fixed: the logit
+ * scale multiplies every logit of its row (scale * q.k + bias); the sink is a
+ * separate logit that joins the softmax normaliser unscaled; the gate
+ * multiplies the normalised output; with e4m3 K/V the keys and values used are
+ * the dequantised ones. A NULL `options`, or one with every pointer NULL and
+ * kv_e4m3 = 0, is the plain call (rba_prefill, rba_prefill_relproj without
+ * sink and gate, rba_decode, rba_decode_split).
+ */
+typedef struct rba_call_options {
+    const float* sink;         /* device fp32 [rows, Hq] or NULL (rows: total_q or batch * n_q)  */
+    const float* gate;         /* device fp32 [rows, Hq] or NULL                                  */
+    const float* logit_scale;  /* device fp32 [rows] or NULL; finite values                       */
+    int32_t kv_e4m3;           /* 0: bf16 K/V; 1: e4m3 K/V (decode only, RBA_ERR_UNSUPPORTED for  */
+                               /* the prefill); other values RBA_ERR_SHAPE                        */
+    float k_scale, v_scale;    /* with kv_e4m3 = 1: dequantization scales (finite, > 0)           */
+} rba_call_options;
+
+/* rba_prefill with options (sink, gate, logit_scale). Other arguments and
+ * errors as rba_prefill; sink, gate and logit_scale must be 4-byte aligned. */
+int rba_prefill_ex(const rba_attn_params* params,
+                   const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                   const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                   const rba_call_options* options, float* out, float* lse, void* stream);
+
+/* rba_prefill_relproj with options (sink, gate, logit_scale; the scale also
+ * multiplies the bias made in the kernel). Other arguments and errors as
+ * rba_prefill_relproj. */
+int rba_prefill_relproj_ex(const rba_attn_params* params,
+                           const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                           const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                           const int32_t* cu_q, const int32_t* seq_lens,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                           const rba_call_options* options, float* out, float* lse, void* stream);
+
+/* rba_decode with options (sink, gate, logit_scale, e4m3 K/V). Other
+ * arguments and errors as rba_decode (and rba_decode_fp8 for the scales). */
+int rba_decode_ex(const rba_attn_params* params,
+                  const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                  const float* rel, const int32_t* seq_lens,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                  void* workspace, size_t workspace_bytes, const rba_call_options* options,
+                  float* out, float* lse, void* stream);
+
+/* rba_decode_split with options (logit_scale, e4m3 K/V). The sink and gate
+ * act in the merge (rba_decode_combine_gated), so they must be NULL here
+ * (RBA_ERR_UNSUPPORTED otherwise). num_splits must be resolved (>= 1). */
+int rba_decode_split_ex(const rba_attn_params* params,
+                        const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                        const float* rel, const int32_t* seq_lens,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                        void* workspace, size_t workspace_bytes, const rba_call_options* options,
+                        void* stream);
 
 /*
  * rba_decode without a workspace argument, for callers that cannot allocate

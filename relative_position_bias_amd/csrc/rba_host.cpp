@@ -294,18 +294,65 @@ int rba_validate_prefill(const rba_attn_params* params, const void* q, const voi
                             max_blocks_per_seq, batch, max_q_len, max_seq_len, out, nullptr, &nothing);
 }
 
-static int prefill_impl(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
-                        int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
-                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
-                        int32_t max_seq_len, const float* sink, const float* gate, const float* lscale, float* out,
-                        float* lse, void* stream) {
-    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// The optional terms of a call, resolved from rba_call_options (NULL: none).
+struct Opts {
+    const float* sink = nullptr;
+    const float* gate = nullptr;
+    const float* lscale = nullptr;
+    bool kv8 = false;
+    float k_scale = 1.f, v_scale = 1.f;
+};
+
+int check_kv_scales(float k_scale, float v_scale) {
+    if (!(k_scale > 0.f && k_scale < INFINITY) || !(v_scale > 0.f && v_scale < INFINITY))
+        return fail(RBA_ERR_SHAPE, "k_scale %g / v_scale %g must be finite and > 0", (double)k_scale,
+                    (double)v_scale);
+    return RBA_OK;
+}
+
+int check_opts(const Opts& o) {
+    if (!aligned4(o.sink) || !aligned4(o.gate) || !aligned4(o.lscale))
+        return fail(RBA_ERR_UNSUPPORTED, "sink/gate/logit_scale must be 4-byte aligned");
+    return o.kv8 ? check_kv_scales(o.k_scale, o.v_scale) : RBA_OK;
+}
+
+int read_options(const rba_call_options* in, bool decode, Opts* o) {
+    *o = Opts();
+    if (in == nullptr) return RBA_OK;
+    if (in->kv_e4m3 != 0 && in->kv_e4m3 != 1)
+        return fail(RBA_ERR_SHAPE, "kv_e4m3 %d must be 0 or 1", in->kv_e4m3);
+    if (in->kv_e4m3 && !decode) return fail(RBA_ERR_UNSUPPORTED, "e4m3 K/V caches are supported by the decode only");
+    o->sink = in->sink;
+    o->gate = in->gate;
+    o->lscale = in->logit_scale;
+    o->kv8 = in->kv_e4m3 == 1;
+    o->k_scale = in->k_scale;
+    o->v_scale = in->v_scale;
+    return RBA_OK;
+}
+
+void tile_shape(rba::PrefillArgs& a, int32_t max_q_len) {
+    a.hpw = prefill_hpw(a.G);
+    a.QT = 32 * (8 / a.hpw);
+    a.n_qt = (int32_t)ceil_div(max_q_len, a.QT);
+    a.n_hc = a.G / a.hpw;
+}
+
+int prefill_impl(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                 int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                 int32_t max_seq_len, const Opts& o, float* out, float* lse, void* stream) {
+    int rc = check_opts(o);
+    if (rc) return rc;
     bool nothing;
-    int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
-                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing);
+    rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                          max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing);
     if (rc || nothing) return rc;
     rba::PrefillArgs a;
-    const int G = params->num_heads_q / params->num_heads_kv;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_cache);
     a.v = static_cast<const uint16_t*>(v_cache);
@@ -313,30 +360,146 @@ static int prefill_impl(const rba_attn_params* params, const void* q, const void
     a.r = nullptr;
     a.proj = nullptr;
     a.proj_heads = 0;
-    a.lscale = lscale;
+    a.lscale = o.lscale;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;
     a.tables = block_tables;
     a.out = out;
     a.lse = lse;
-    a.sink = sink;
-    a.gate = gate;
+    a.sink = o.sink;
+    a.gate = o.gate;
     a.num_blocks = num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.batch = batch;
     a.Hq = params->num_heads_q;
     a.Hkv = params->num_heads_kv;
-    a.G = G;
+    a.G = params->num_heads_q / params->num_heads_kv;
     a.R = params->rel_extent;
     a.W = params->window;
     a.c1 = (float)((double)params->scale * 1.4426950408889634);
-    a.hpw = prefill_hpw(G);
-    a.QT = 32 * (8 / a.hpw);
-    a.n_qt = (int32_t)ceil_div(max_q_len, a.QT);
-    a.n_hc = G / a.hpw;
+    tile_shape(a, max_q_len);
     hipError_t e = rba::launch_prefill(a, params->head_dim_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
+}
+
+int relproj_impl(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                 int32_t num_blocks, const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                 const int32_t* cu_q, const int32_t* seq_lens, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len, int32_t max_seq_len, const Opts& o,
+                 float* out, float* lse, void* stream) {
+    int rc = check_opts(o);
+    if (rc) return rc;
+    bool nothing;
+    rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
+                          max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r", true);
+    if (rc || nothing) return rc;
+    if (d_r != 64) return fail(RBA_ERR_UNSUPPORTED, "d_r %d: only 64 is supported", d_r);
+    if (proj_heads != 1 && proj_heads != params->num_heads_q)
+        return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, params->num_heads_q);
+    if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
+    if (!aligned16(rel_proj)) return fail(RBA_ERR_UNSUPPORTED, "rel_proj must be 16-byte aligned");
+    rba::PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.rel = nullptr;
+    a.r = static_cast<const uint16_t*>(r);
+    a.proj = static_cast<const uint16_t*>(rel_proj);
+    a.proj_heads = proj_heads;
+    a.lscale = o.lscale;
+    a.cu_q = cu_q;
+    a.seq_lens = seq_lens;
+    a.tables = block_tables;
+    a.out = out;
+    a.lse = lse;
+    a.sink = o.sink;
+    a.gate = o.gate;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.batch = batch;
+    a.Hq = params->num_heads_q;
+    a.Hkv = params->num_heads_kv;
+    a.G = params->num_heads_q / params->num_heads_kv;
+    a.R = params->rel_extent;
+    a.W = params->window;
+    a.c1 = (float)((double)params->scale * 1.4426950408889634);
+    tile_shape(a, max_q_len);
+    hipError_t e = rba::launch_prefill_relproj(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
+// Split stage, then (if `combine`) the merge with the sink and gate. A split
+// alone needs a resolved num_splits and takes no sink or gate (they act in
+// the merge). `need_lscale`: a missing logit_scale is an error (the
+// dedicated log-position entry point).
+int decode_impl(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                void* workspace, size_t workspace_bytes, const Opts& o, bool combine, bool need_lscale, float* out,
+                float* lse, void* stream, const char* name) {
+    if (!combine && num_splits < 1) return fail(RBA_ERR_SHAPE, "%s needs a resolved num_splits >= 1", name);
+    if (!combine && (o.sink != nullptr || o.gate != nullptr))
+        return fail(RBA_ERR_UNSUPPORTED, "%s: sink and gate act in the combine (rba_decode_combine_gated)", name);
+    int rc = check_opts(o);
+    if (rc) return rc;
+    bool nothing;
+    int32_t splits = 0;
+    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                         batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, out, lse, combine, &splits,
+                         &nothing);
+    if (rc || nothing) return rc;
+    if (need_lscale && o.lscale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
+    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+    if (o.kv8) {
+        a.c1 = (float)((double)params->scale * (double)o.k_scale * 1.4426950408889634);
+        a.v_scale = o.v_scale;
+        a.kv8 = 1;
+    }
+    a.lscale = o.lscale;
+    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode split launch");
+    if (!combine) return ok();
+    return rba_decode_combine_gated(params, batch, n_q, splits, workspace, workspace_bytes, o.sink, o.gate, out,
+                                    lse, stream);
+}
+
+Opts gated_opts(const float* sink, const float* gate) {
+    Opts o;
+    o.sink = sink;
+    o.gate = gate;
+    return o;
+}
+
+Opts lscale_opts(const float* logit_scale) {
+    Opts o;
+    o.lscale = logit_scale;
+    return o;
+}
+
+Opts fp8_opts(float k_scale, float v_scale) {
+    Opts o;
+    o.kv8 = true;
+    o.k_scale = k_scale;
+    o.v_scale = v_scale;
+    return o;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rba_prefill_ex(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                   int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
+                   int32_t max_seq_len, const rba_call_options* options, float* out, float* lse, void* stream) {
+    Opts o;
+    int rc = read_options(options, false, &o);
+    if (rc) return rc;
+    return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, o, out, lse, stream);
 }
 
 int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -345,7 +508,8 @@ int rba_prefill_gated(const rba_attn_params* params, const void* q, const void* 
                       int32_t max_seq_len, const float* sink, const float* gate, float* out, float* lse,
                       void* stream) {
     return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
-                        max_blocks_per_seq, batch, max_q_len, max_seq_len, sink, gate, nullptr, out, lse, stream);
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, gated_opts(sink, gate), out, lse,
+                        stream);
 }
 
 int rba_prefill_logpos(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -353,9 +517,8 @@ int rba_prefill_logpos(const rba_attn_params* params, const void* q, const void*
                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
                        int32_t max_seq_len, const float* logit_scale, float* out, float* lse, void* stream) {
     if (batch > 0 && max_q_len > 0 && logit_scale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
-    if (!aligned4(logit_scale)) return fail(RBA_ERR_UNSUPPORTED, "logit_scale must be 4-byte aligned");
     return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
-                        max_blocks_per_seq, batch, max_q_len, max_seq_len, nullptr, nullptr, logit_scale, out, lse,
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, lscale_opts(logit_scale), out, lse,
                         stream);
 }
 
@@ -363,8 +526,20 @@ int rba_prefill(const rba_attn_params* params, const void* q, const void* k_cach
                 int32_t num_blocks, const float* rel, const int32_t* cu_q, const int32_t* seq_lens,
                 const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
                 int32_t max_seq_len, float* out, float* lse, void* stream) {
-    return rba_prefill_gated(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
-                             max_blocks_per_seq, batch, max_q_len, max_seq_len, nullptr, nullptr, out, lse, stream);
+    return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
+                        max_blocks_per_seq, batch, max_q_len, max_seq_len, Opts(), out, lse, stream);
+}
+
+int rba_prefill_relproj_ex(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                           int32_t num_blocks, const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                           const int32_t* cu_q, const int32_t* seq_lens, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                           const rba_call_options* options, float* out, float* lse, void* stream) {
+    Opts o;
+    int rc = read_options(options, false, &o);
+    if (rc) return rc;
+    return relproj_impl(params, q, k_cache, v_cache, num_blocks, r, rel_proj, d_r, proj_heads, cu_q, seq_lens,
+                        block_tables, max_blocks_per_seq, batch, max_q_len, max_seq_len, o, out, lse, stream);
 }
 
 int rba_prefill_relproj(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -372,50 +547,9 @@ int rba_prefill_relproj(const rba_attn_params* params, const void* q, const void
                         const int32_t* cu_q, const int32_t* seq_lens, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len, int32_t max_seq_len,
                         const float* sink, const float* gate, float* out, float* lse, void* stream) {
-    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
-    bool nothing;
-    int rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
-                              max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r",
-                              true);
-    if (rc || nothing) return rc;
-    if (d_r != 64) return fail(RBA_ERR_UNSUPPORTED, "d_r %d: only 64 is supported", d_r);
-    if (proj_heads != 1 && proj_heads != params->num_heads_q)
-        return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, params->num_heads_q);
-    if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
-    if (!aligned16(rel_proj)) return fail(RBA_ERR_UNSUPPORTED, "rel_proj must be 16-byte aligned");
-    rba::PrefillArgs a;
-    const int G = params->num_heads_q / params->num_heads_kv;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k_cache);
-    a.v = static_cast<const uint16_t*>(v_cache);
-    a.rel = nullptr;
-    a.r = static_cast<const uint16_t*>(r);
-    a.proj = static_cast<const uint16_t*>(rel_proj);
-    a.proj_heads = proj_heads;
-    a.lscale = nullptr;
-    a.cu_q = cu_q;
-    a.seq_lens = seq_lens;
-    a.tables = block_tables;
-    a.out = out;
-    a.lse = lse;
-    a.sink = sink;
-    a.gate = gate;
-    a.num_blocks = num_blocks;
-    a.max_blocks = max_blocks_per_seq;
-    a.batch = batch;
-    a.Hq = params->num_heads_q;
-    a.Hkv = params->num_heads_kv;
-    a.G = G;
-    a.R = params->rel_extent;
-    a.W = params->window;
-    a.c1 = (float)((double)params->scale * 1.4426950408889634);
-    a.hpw = prefill_hpw(G);
-    a.QT = 32 * (8 / a.hpw);
-    a.n_qt = (int32_t)ceil_div(max_q_len, a.QT);
-    a.n_hc = G / a.hpw;
-    hipError_t e = rba::launch_prefill_relproj(a, params->head_dim_v, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "prefill launch");
-    return ok();
+    return relproj_impl(params, q, k_cache, v_cache, num_blocks, r, rel_proj, d_r, proj_heads, cu_q, seq_lens,
+                        block_tables, max_blocks_per_seq, batch, max_q_len, max_seq_len, gated_opts(sink, gate), out,
+                        lse, stream);
 }
 
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,
@@ -457,18 +591,22 @@ int rba_decode_split(const rba_attn_params* params, const void* q, const void* k
                      const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
                      int32_t max_seq_len, int32_t num_splits, void* workspace, size_t workspace_bytes,
                      void* stream) {
-    if (num_splits < 1) return fail(RBA_ERR_SHAPE, "rba_decode_split needs a resolved num_splits >= 1");
-    bool nothing;
-    int32_t splits = 0;
-    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
-                             workspace_bytes, nullptr, nullptr, false, &splits, &nothing);
-    if (rc || nothing) return rc;
-    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return ok();
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, Opts(), false, false, nullptr,
+                       nullptr, stream, "rba_decode_split");
+}
+
+int rba_decode_split_ex(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes, const rba_call_options* options,
+                        void* stream) {
+    Opts o;
+    int rc = read_options(options, true, &o);
+    if (rc) return rc;
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, o, false, false, nullptr,
+                       nullptr, stream, "rba_decode_split_ex");
 }
 
 int rba_decode_combine_gated(const rba_attn_params* params, int32_t batch, int32_t n_q, int32_t num_splits,
@@ -513,18 +651,22 @@ int rba_decode(const rba_attn_params* params, const void* q, const void* k_cache
                int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
                int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
                void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
-    bool nothing;
-    int32_t splits = 0;
-    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
-                             workspace_bytes, out, lse, true, &splits, &nothing);
-    if (rc || nothing) return rc;
-    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, Opts(), true, false, out, lse,
+                       stream, "rba_decode");
+}
+
+int rba_decode_ex(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                  int32_t num_blocks, const float* rel, const int32_t* seq_lens, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                  void* workspace, size_t workspace_bytes, const rba_call_options* options, float* out, float* lse,
+                  void* stream) {
+    Opts o;
+    int rc = read_options(options, true, &o);
+    if (rc) return rc;
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, o, true, false, out, lse,
+                       stream, "rba_decode_ex");
 }
 
 int rba_decode_noalloc(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -560,20 +702,9 @@ int rba_decode_gated(const rba_attn_params* params, const void* q, const void* k
                      int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
                      int32_t num_splits, void* workspace, size_t workspace_bytes, const float* sink,
                      const float* gate, float* out, float* lse, void* stream) {
-    if (!aligned4(sink) || !aligned4(gate)) return fail(RBA_ERR_UNSUPPORTED, "sink/gate must be 4-byte aligned");
-    bool nothing;
-    int32_t splits = 0;
-    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
-                             workspace_bytes, out, lse, true, &splits, &nothing);
-    if (rc || nothing) return rc;
-    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return rba_decode_combine_gated(params, batch, n_q, splits, workspace, workspace_bytes, sink, gate, out, lse,
-                                    stream);
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, gated_opts(sink, gate), true,
+                       false, out, lse, stream, "rba_decode_gated");
 }
 
 int rba_decode_logpos(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -581,35 +712,9 @@ int rba_decode_logpos(const rba_attn_params* params, const void* q, const void* 
                       int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
                       int32_t num_splits, void* workspace, size_t workspace_bytes, const float* logit_scale,
                       float* out, float* lse, void* stream) {
-    bool nothing;
-    int32_t splits = 0;
-    int rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                             max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
-                             workspace_bytes, out, lse, true, &splits, &nothing);
-    if (rc || nothing) return rc;
-    if (logit_scale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
-    if (!aligned4(logit_scale)) return fail(RBA_ERR_UNSUPPORTED, "logit_scale must be 4-byte aligned");
-    rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
-    a.lscale = logit_scale;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
-}
-
-static int check_kv_scales(float k_scale, float v_scale) {
-    if (!(k_scale > 0.f && k_scale < INFINITY) || !(v_scale > 0.f && v_scale < INFINITY))
-        return fail(RBA_ERR_SHAPE, "k_scale %g / v_scale %g must be finite and > 0", (double)k_scale,
-                    (double)v_scale);
-    return RBA_OK;
-}
-
-static rba::DecodeArgs fp8_args(rba::DecodeArgs a, const rba_attn_params* p, float k_scale, float v_scale) {
-    a.c1 = (float)((double)p->scale * (double)k_scale * 1.4426950408889634);
-    a.v_scale = v_scale;
-    a.kv8 = 1;
-    return a;
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, lscale_opts(logit_scale),
+                       true, true, out, lse, stream, "rba_decode_logpos");
 }
 
 int rba_decode_split_fp8(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -617,21 +722,9 @@ int rba_decode_split_fp8(const rba_attn_params* params, const void* q, const voi
                          const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
                          int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits, void* workspace,
                          size_t workspace_bytes, void* stream) {
-    if (num_splits < 1) return fail(RBA_ERR_SHAPE, "rba_decode_split_fp8 needs a resolved num_splits >= 1");
-    int rc = check_kv_scales(k_scale, v_scale);
-    if (rc) return rc;
-    bool nothing;
-    int32_t splits = 0;
-    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
-                         batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, nullptr, nullptr, false,
-                         &splits, &nothing);
-    if (rc || nothing) return rc;
-    rba::DecodeArgs a = fp8_args(decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                             max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace),
-                                 params, k_scale, v_scale);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return ok();
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, fp8_opts(k_scale, v_scale),
+                       false, false, nullptr, nullptr, stream, "rba_decode_split_fp8");
 }
 
 int rba_decode_fp8(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
@@ -639,21 +732,9 @@ int rba_decode_fp8(const rba_attn_params* params, const void* q, const void* k_c
                    const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
                    int32_t max_seq_len, int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
                    float* lse, void* stream) {
-    int rc = check_kv_scales(k_scale, v_scale);
-    if (rc) return rc;
-    bool nothing;
-    int32_t splits = 0;
-    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
-                         batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, out, lse, true, &splits,
-                         &nothing);
-    if (rc || nothing) return rc;
-    rba::DecodeArgs a = fp8_args(decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                             max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace),
-                                 params, k_scale, v_scale);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = rba::launch_decode_split(a, params->head_dim_v, s);
-    if (e != hipSuccess) return hip_fail(e, "decode split launch");
-    return rba_decode_combine(params, batch, n_q, splits, workspace, workspace_bytes, out, lse, stream);
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, fp8_opts(k_scale, v_scale),
+                       true, false, out, lse, stream, "rba_decode_fp8");
 }
 
 }  // extern "C"

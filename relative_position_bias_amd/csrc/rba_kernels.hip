@@ -780,8 +780,8 @@ __global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A
 constexpr int DR = 64;       // width of r
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
-template <int DV>
-__global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
+template <int DV, bool LS>
+__device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     constexpr int NW = 8;   // every wave issues copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
@@ -817,6 +817,8 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
     const int r = qa + n;
     const bool real = r < q_len;
     const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
+    const float fls = (LS && real) ? A.lscale[q_start + r] : 1.f;  // the row's logit scale
+    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
 
     Cols<DV> C;
     C.pos = real ? ctx + r : -1;
@@ -944,7 +946,7 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
         RelVals rb;
         if (biased) read_bias(js, rb);
         float x[16];
-        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, A.c1, LOG2E, lane, x);
+        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, c1f, l2f, lane, x);
         if (__any(!C.m_set || sm_trigger(C, M))) {
             if (__any(!C.m_set)) sm_init_ref(C, M, x);
             if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
@@ -1031,6 +1033,16 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
     if (!wave_active || !real) return;
     store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
               A.gate ? A.gate[trow] : INFINITY, lane);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
+    prefill_relproj_body<DV, false>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_relproj_logpos_kernel(const PrefillArgs A) {
+    prefill_relproj_body<DV, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1421,9 +1433,14 @@ __global__ void __launch_bounds__(512) decode_split8_kernel(const DecodeArgs A) 
     decode_split_body<DV, KV8, false, 8>(A);
 }
 
-template <int DV>
+template <int DV, bool KV8>
 __global__ void __launch_bounds__(256, 2) decode_split_logpos_kernel(const DecodeArgs A) {
-    decode_split_body<DV, false, true>(A);
+    decode_split_body<DV, KV8, true>(A);
+}
+
+template <int DV, bool KV8>
+__global__ void __launch_bounds__(512) decode_split8_logpos_kernel(const DecodeArgs A) {
+    decode_split_body<DV, KV8, true, 8>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1747,9 +1764,9 @@ __global__ void __launch_bounds__(256, 2) decode16_split_kernel(const DecodeArgs
     decode16_split_body<DV, KV8, false>(A);
 }
 
-template <int DV>
+template <int DV, bool KV8>
 __global__ void __launch_bounds__(256, 2) decode16_split_logpos_kernel(const DecodeArgs A) {
-    decode16_split_body<DV, false, true>(A);
+    decode16_split_body<DV, KV8, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1864,48 +1881,62 @@ hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
-    if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((prefill_relproj_kernel<64>), g, blk, 0, s, a);
+    if (a.lscale != nullptr) {  // per-row logit scale
+        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_logpos_kernel<128>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_logpos_kernel<64>), g, blk, 0, s, a);
+    } else {
+        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_kernel<64>), g, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
+
+namespace {
+
+// Kernel choice for one (dv, K/V type, scale flag). G * n_q <= 16: the
+// 16-column kernel (one group, n_cg == 1). dv 64 over e4m3 K/V when the grid
+// fits one workgroup per CU: 8-wave workgroups (for bf16 K/V a second block
+// in flight measured no faster, so the 4-wave kernel runs there). Otherwise
+// the 32-column kernel.
+template <int DV, bool KV8, bool LS>
+void launch_split_t(const DecodeArgs& a, dim3 g, hipStream_t s) {
+    const dim3 blk(256);
+    if (a.G * a.n_q <= 16) {
+        if (LS) hipLaunchKernelGGL((decode16_split_logpos_kernel<DV, KV8>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((decode16_split_kernel<DV, KV8>), g, blk, 0, s, a);
+        return;
+    }
+    if constexpr (DV == 64 && KV8) {
+        if (a.wide) {
+            if (LS) hipLaunchKernelGGL((decode_split8_logpos_kernel<DV, KV8>), g, dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((decode_split8_kernel<DV, KV8>), g, dim3(512), 0, s, a);
+            return;
+        }
+    }
+    if (LS) hipLaunchKernelGGL((decode_split_logpos_kernel<DV, KV8>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<DV, KV8>), g, blk, 0, s, a);
+}
+
+template <bool LS>
+void launch_split_ls(const DecodeArgs& a, int dv, dim3 g, hipStream_t s) {
+    const bool kv8 = a.kv8 != 0;
+    if (dv == 128) {
+        if (kv8) launch_split_t<128, true, LS>(a, g, s);
+        else launch_split_t<128, false, LS>(a, g, s);
+    } else {
+        if (kv8) launch_split_t<64, true, LS>(a, g, s);
+        else launch_split_t<64, false, LS>(a, g, s);
+    }
+}
+
+}  // namespace
 
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.Hkv * a.n_cg * a.splits;
     if (grid <= 0) return hipSuccess;
-    const dim3 g((unsigned)grid), blk(256);
-    const bool kv8 = a.kv8 != 0;
-    if (a.lscale != nullptr) {  // per-row logit scale (bf16 K/V only)
-        if (a.G * a.n_q <= 16) {
-            if (dv == 128) hipLaunchKernelGGL((decode16_split_logpos_kernel<128>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((decode16_split_logpos_kernel<64>), g, blk, 0, s, a);
-        } else {
-            if (dv == 128) hipLaunchKernelGGL((decode_split_logpos_kernel<128>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((decode_split_logpos_kernel<64>), g, blk, 0, s, a);
-        }
-        return hipGetLastError();
-    }
-    if (a.G * a.n_q <= 16) {  // one 16-column group (n_cg == 1)
-        if (dv == 128) {
-            if (kv8) hipLaunchKernelGGL((decode16_split_kernel<128, true>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((decode16_split_kernel<128, false>), g, blk, 0, s, a);
-        } else {
-            if (kv8) hipLaunchKernelGGL((decode16_split_kernel<64, true>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((decode16_split_kernel<64, false>), g, blk, 0, s, a);
-        }
-        return hipGetLastError();
-    }
-    if (dv == 128) {
-        if (kv8) hipLaunchKernelGGL((decode_split_kernel<128, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((decode_split_kernel<128, false>), g, blk, 0, s, a);
-    } else if (a.wide && kv8) {
-        // at most one workgroup per CU: 8 waves each. (For bf16 K/V the
-        // second block in flight measured no faster, so the 4-wave kernel
-        // runs there.)
-        hipLaunchKernelGGL((decode_split8_kernel<64, true>), g, dim3(512), 0, s, a);
-    } else {
-        if (kv8) hipLaunchKernelGGL((decode_split_kernel<64, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((decode_split_kernel<64, false>), g, blk, 0, s, a);
-    }
+    const dim3 g((unsigned)grid);
+    if (a.lscale != nullptr) launch_split_ls<true>(a, dv, g, s);  // per-row logit scale
+    else launch_split_ls<false>(a, dv, g, s);
     return hipGetLastError();
 }
 

@@ -43,6 +43,18 @@ class AttnParams(ctypes.Structure):
     ]
 
 
+class CallOptions(ctypes.Structure):
+    """Mirror of rba_call_options in include/rba.h."""
+    _fields_ = [
+        ("sink", _ptr),
+        ("gate", _ptr),
+        ("logit_scale", _ptr),
+        ("kv_e4m3", _i32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+    ]
+
+
 class RbaError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"librba error {code}: {msg}")
@@ -88,6 +100,18 @@ _SIGNATURES = {
                                             _ptr, _size, _ptr]),
     "rba_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
                                           _i32, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr]),
+    "rba_prefill_ex": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                      _ptr, _i32, _i32, _i32, _i32, ctypes.POINTER(CallOptions), _ptr, _ptr,
+                                      _ptr]),
+    "rba_prefill_relproj_ex": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr,
+                                              _i32, _i32, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32,
+                                              ctypes.POINTER(CallOptions), _ptr, _ptr, _ptr]),
+    "rba_decode_ex": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr, _i32,
+                                     _i32, _i32, _i32, _i32, _ptr, _size, ctypes.POINTER(CallOptions), _ptr, _ptr,
+                                     _ptr]),
+    "rba_decode_split_ex": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
+                                           _i32, _i32, _i32, _i32, _i32, _ptr, _size,
+                                           ctypes.POINTER(CallOptions), _ptr]),
 }
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # RBA_NOALLOC_SCRATCH_BYTES in include/rba.h
@@ -174,6 +198,25 @@ def _opt(t: Optional[torch.Tensor], name: str, shape) -> Optional[int]:
     return _dev(t, torch.float32, name)
 
 
+def call_options(rows: int, Hq: int, sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                 logit_scale: Optional[torch.Tensor] = None,
+                 kv_scales: Optional[Tuple[float, float]] = None) -> Optional[CallOptions]:
+    """rba_call_options for the given optional terms (None if there are
+    none): sink / gate fp32 [rows, Hq], logit_scale fp32 [rows], kv_scales =
+    (k_scale, v_scale) for e4m3 caches."""
+    if sink is None and gate is None and logit_scale is None and kv_scales is None:
+        return None
+    if logit_scale is not None and tuple(logit_scale.shape) != (rows,):
+        raise ValueError(f"logit_scale must be [{rows}]")
+    o = CallOptions()
+    o.sink = _opt(sink, "sink", (rows, Hq))
+    o.gate = _opt(gate, "gate", (rows, Hq))
+    o.logit_scale = _dev(logit_scale, torch.float32, "logit_scale") if logit_scale is not None else None
+    o.kv_e4m3 = 1 if kv_scales is not None else 0
+    o.k_scale, o.v_scale = (float(kv_scales[0]), float(kv_scales[1])) if kv_scales is not None else (1.0, 1.0)
+    return o
+
+
 def _prefill_batch(cu_q, seq_lens) -> int:
     """Sequence count of a prefill call: cu_q holds batch + 1 offsets and
     seq_lens one length per sequence."""
@@ -195,8 +238,8 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     v_cache [nb, Hkv, 128, dv] bf16; rel [total_q, Hq, R] fp32; cu_q [B+1],
     seq_lens [B], block_tables [B, max_blocks] int32. max_q_len / max_seq_len
     are host-side bounds (no device read happens here). With sink and/or gate
-    (fp32 [total_q, Hq]) rba_prefill_gated runs; with logit_scale (fp32
-    [total_q]) rba_prefill_logpos."""
+    (fp32 [total_q, Hq]) and/or logit_scale (fp32 [total_q]), in any
+    combination, rba_prefill_ex runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -212,36 +255,18 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     _shape(out, (total_q, Hq, dv), "out")
     _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
-    if logit_scale is not None:
-        if sink is not None or gate is not None:
-            raise ValueError("logit_scale cannot be combined with sink / gate")
-        if tuple(logit_scale.shape) != (total_q,):
-            raise ValueError("logit_scale must be [total_q]")
-        _check(lib().rba_prefill_logpos(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
             _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
             _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
             _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
-            int(max_seq_len), _dev(logit_scale, torch.float32, "logit_scale"), _dev(out, torch.float32, "out"),
-            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
-        return out, lse
-    if sink is not None or gate is not None:
-        _check(lib().rba_prefill_gated(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-            _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
-            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
-            int(max_seq_len), _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
-            _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
-            _stream(stream)))
-        return out, lse
-    _check(lib().rba_prefill(
-        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-        _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
-        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
-        int(max_seq_len), _dev(out, torch.float32, "out"),
-        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+            int(max_seq_len))
+    tail = (_dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream))
+    opts = call_options(total_q, Hq, sink, gate, logit_scale)
+    if opts is None:
+        _check(lib().rba_prefill(*args, *tail))
+    else:
+        _check(lib().rba_prefill_ex(*args, ctypes.byref(opts), *tail))
     return out, lse
 
 
@@ -249,10 +274,12 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
                     max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, want_lse: bool = False,
                     sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                    logit_scale: Optional[torch.Tensor] = None,
                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill_relproj: as prefill, with the bias made in the kernel from
     r [total_q, Hq, 64] bf16 and proj [1 or Hq, R, 64] bf16 (rel_logits_proj
-    in linear-weight layout; R = proj.shape[1])."""
+    in linear-weight layout; R = proj.shape[1]). With logit_scale (fp32
+    [total_q]) rba_prefill_relproj_ex runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -271,15 +298,20 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
     _shape(out, (total_q, Hq, dv), "out")
     _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
-    _check(lib().rba_prefill_relproj(
-        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(r, torch.bfloat16, "r"),
-        _dev(proj, torch.bfloat16, "proj"), d_r, proj_heads,
-        _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
-        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
-        int(max_seq_len), _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
-        _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
-        _stream(stream)))
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(r, torch.bfloat16, "r"),
+            _dev(proj, torch.bfloat16, "proj"), d_r, proj_heads,
+            _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
+            int(max_seq_len))
+    tail = (_dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream))
+    if logit_scale is None:
+        _check(lib().rba_prefill_relproj(*args, _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
+                                         *tail))
+    else:
+        opts = call_options(total_q, Hq, sink, gate, logit_scale)
+        _check(lib().rba_prefill_relproj_ex(*args, ctypes.byref(opts), *tail))
     return out, lse
 
 
@@ -330,10 +362,10 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_decode (split-KV + combine). q [batch*n_q, Hq, 128] bf16; rel
     [batch*n_q, Hq, R] fp32. `workspace` (uint8, on the GPU) is allocated with
-    torch if not given. With kv_scales = (k_scale, v_scale) the caches are
-    e4m3 bytes and rba_decode_fp8 runs. With sink and/or gate (fp32
-    [batch*n_q, Hq]) the merge is rba_decode_combine_gated. With logit_scale
-    (fp32 [batch*n_q]; bf16 caches, no sink / gate) rba_decode_logpos runs."""
+    torch if not given. Optional terms, in any combination (rba_decode_ex):
+    kv_scales = (k_scale, v_scale) for e4m3 caches (uint8 or
+    torch.float8_e4m3fn), sink and/or gate (fp32 [batch*n_q, Hq]) and
+    logit_scale (fp32 [batch*n_q])."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
     L = lib()
@@ -346,84 +378,43 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
     _shape(out, (rows, Hq, dv), "out")
     _shape(lse, (rows, Hq), "lse")
-    if logit_scale is not None:
-        if sink is not None or gate is not None or kv_scales is not None:
-            raise ValueError("logit_scale cannot be combined with sink / gate / kv_scales")
-        if tuple(logit_scale.shape) != (rows,):
-            raise ValueError("logit_scale must be [batch * n_q]")
-        _check(L.rba_decode_logpos(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-            _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
-            block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
-            _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
-            _dev(logit_scale, torch.float32, "logit_scale"), _dev(out, torch.float32, "out"),
-            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
-        return out, lse
-    if sink is not None or gate is not None:
-        splits = int(num_splits) or plan_splits(Hq, p.num_heads_kv, dv, p.rel_extent, window, scale, batch, n_q,
-                                                int(max_seq_len), _num_cus(q.device))
-        if kv_scales is not None:
-            decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q=n_q, window=window, scale=scale,
-                         max_seq_len=max_seq_len, num_splits=splits, workspace=workspace, kv_scales=kv_scales,
-                         stream=stream)
-            _check(L.rba_decode_combine_gated(
-                ctypes.byref(p), batch, n_q, splits, _dev(workspace, torch.uint8, "workspace"),
-                workspace.numel(), _opt(sink, "sink", (rows, Hq)), _opt(gate, "gate", (rows, Hq)),
-                _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
-                _stream(stream)))
-            return out, lse
-        _check(L.rba_decode_gated(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-            _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
-            block_tables.shape[1], batch, n_q, int(max_seq_len), splits,
-            _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _opt(sink, "sink", (rows, Hq)),
-            _opt(gate, "gate", (rows, Hq)), _dev(out, torch.float32, "out"),
-            _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
-        return out, lse
-    if kv_scales is not None:
-        _check(L.rba_decode_fp8(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(_kv8(k_cache), torch.uint8, "k_cache"),
-            _dev(_kv8(v_cache), torch.uint8, "v_cache"), nb, float(kv_scales[0]), float(kv_scales[1]),
+    k8 = _kv8(k_cache) if kv_scales is not None else k_cache
+    v8 = _kv8(v_cache) if kv_scales is not None else v_cache
+    kvt = torch.uint8 if kv_scales is not None else torch.bfloat16
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k8, kvt, "k_cache"), _dev(v8, kvt, "v_cache"), nb,
             _dev(rel, torch.float32, "rel"), _dev(seq_lens, torch.int32, "seq_lens"),
-            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q,
-            int(max_seq_len), int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
-            _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
-            _stream(stream)))
-        return out, lse
-    _check(L.rba_decode(
-        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
-        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
-        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _dev(out, torch.float32, "out"),
-        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q, int(max_seq_len),
+            int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    tail = (_dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
+            _stream(stream))
+    opts = call_options(rows, Hq, sink, gate, logit_scale, kv_scales)
+    if opts is None:
+        _check(L.rba_decode(*args, *tail))
+    else:
+        _check(L.rba_decode_ex(*args, ctypes.byref(opts), *tail))
     return out, lse
 
 
 def decode_split(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window: int, scale: float,
                  max_seq_len: int, num_splits: int, workspace: torch.Tensor,
-                 kv_scales: Optional[Tuple[float, float]] = None, stream=None) -> None:
+                 kv_scales: Optional[Tuple[float, float]] = None, logit_scale: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
     """rba_decode_split: partial outputs of every split into `workspace`
-    (rba_decode_split_fp8 with kv_scales, e4m3 caches)."""
+    (rba_decode_split_ex with kv_scales (e4m3 caches) and/or logit_scale)."""
     p, batch, rows, Hq, dv, nb = _decode_common(q, k_cache, v_cache, rel, seq_lens, block_tables, n_q,
                                                 window, scale)
-    if kv_scales is not None:
-        _check(lib().rba_decode_split_fp8(
-            ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(_kv8(k_cache), torch.uint8, "k_cache"),
-            _dev(_kv8(v_cache), torch.uint8, "v_cache"), nb, float(kv_scales[0]), float(kv_scales[1]),
+    k8 = _kv8(k_cache) if kv_scales is not None else k_cache
+    v8 = _kv8(v_cache) if kv_scales is not None else v_cache
+    kvt = torch.uint8 if kv_scales is not None else torch.bfloat16
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k8, kvt, "k_cache"), _dev(v8, kvt, "v_cache"), nb,
             _dev(rel, torch.float32, "rel"), _dev(seq_lens, torch.int32, "seq_lens"),
-            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q,
-            int(max_seq_len), int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
-            _stream(stream)))
-        return
-    _check(lib().rba_decode_split(
-        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-        _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
-        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
-        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits),
-        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+            _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, n_q, int(max_seq_len),
+            int(num_splits), _dev(workspace, torch.uint8, "workspace"), workspace.numel())
+    opts = call_options(rows, Hq, logit_scale=logit_scale, kv_scales=kv_scales)
+    if opts is None:
+        _check(lib().rba_decode_split(*args, _stream(stream)))
+    else:
+        _check(lib().rba_decode_split_ex(*args, ctypes.byref(opts), _stream(stream)))
 
 
 def decode_combine(*, Hq: int, Hkv: int, dv: int, rel_extent: int, window: int, scale: float, batch: int,

@@ -260,3 +260,59 @@ def test_logpos_rejects_missing_or_misaligned_scale():
     rc = lib.rba_decode_logpos(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, 8, P, 1 << 30, P + 2,
                                P, None, None)
     assert rc == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_options_are_checked_before_any_launch():
+    """rba_*_ex: the options struct is read and checked on the host first."""
+    lib = rba.lib()
+    p = prm()
+    d = dprm()
+
+    def opts(**kw):
+        o = rba.CallOptions()
+        o.k_scale = o.v_scale = 1.0
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return ctypes.byref(o)
+
+    def pre(o, batch=1):
+        return lib.rba_prefill_ex(ctypes.byref(p), P, P, P, 64, P, P, P, P, 64, batch, 8192, 8192, o, P, None, None)
+
+    def rel(o):
+        return lib.rba_prefill_relproj_ex(ctypes.byref(p), P, P, P, 64, P, P, 64, 1, P, P, P, 64, 1, 8192, 8192, o,
+                                          P, None, None)
+
+    def dec(o, splits=0):
+        return lib.rba_decode_ex(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, splits, P, 1 << 30,
+                                 o, P, None, None)
+
+    def split(o, splits=8):
+        return lib.rba_decode_split_ex(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, splits, P,
+                                       1 << 30, o, None)
+
+    assert pre(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED      # e4m3 caches: decode only
+    assert rel(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED
+    assert pre(opts(kv_e4m3=2)) == rba.RBA_ERR_SHAPE
+    assert dec(opts(kv_e4m3=-1)) == rba.RBA_ERR_SHAPE
+    for field in ("sink", "gate", "logit_scale"):
+        assert pre(opts(**{field: P + 2})) == rba.RBA_ERR_UNSUPPORTED, field
+        assert dec(opts(**{field: P + 2})) == rba.RBA_ERR_UNSUPPORTED, field
+    for ks, vs in ((0.0, 1.0), (1.0, float("nan")), (float("inf"), 1.0)):
+        assert dec(opts(kv_e4m3=1, k_scale=ks, v_scale=vs)) == rba.RBA_ERR_SHAPE
+        assert split(opts(kv_e4m3=1, k_scale=ks, v_scale=vs)) == rba.RBA_ERR_SHAPE
+    assert split(opts(sink=P)) == rba.RBA_ERR_UNSUPPORTED         # sink / gate act in the combine
+    assert "combine" in rba.last_error()
+    assert split(opts(gate=P)) == rba.RBA_ERR_UNSUPPORTED
+    assert split(None, splits=0) == rba.RBA_ERR_SHAPE             # resolved split count needed
+    assert pre(opts(kv_e4m3=1), batch=0) == rba.RBA_ERR_UNSUPPORTED
+    assert pre(opts(sink=P, gate=P, logit_scale=P), batch=0) == rba.RBA_OK   # empty call, no launch
+
+
+def test_call_options_marshalling():
+    """The binding's options struct matches the header's field order."""
+    names = [f[0] for f in rba.CallOptions._fields_]
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct rba_call_options \{(.*?)\} rba_call_options;", text, re.S).group(1)
+    declared = re.findall(r"\b(\w+)\s*[;,]", body)
+    assert declared == names
+    assert rba.call_options(4, 2) is None
