@@ -1100,30 +1100,31 @@ __device__ __forceinline__ void store_v_sub(__bf16* Vw, const VSub<DV>& v, int l
     }
 }
 
-// e4m3 (OCP FP8) K/V. A cache element is one byte; gfx950's
-// v_cvt_pk_f32_fp8 decodes e4m3 to fp32, and every e4m3 value (3 mantissa
-// bits, exponents 2^-9 .. 2^8) is exact in bf16, so the MFMAs see exactly the
-// stored values. The dequantization scales are folded into the score scale
-// (K) and the split outputs (V).
+// e4m3 (OCP FP8) K/V. A cache element is one byte. Every e4m3 value (3
+// mantissa bits, exponents 2^-9 .. 2^8) is exact in bf16, so widening to bf16
+// loses nothing and the MFMAs see exactly the stored values. The
+// dequantization scales are folded into the score scale (K) and the split
+// outputs (V).
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// 8 e4m3 values (lowest address first) as 8 bf16.
+// 8 e4m3 values (lowest address first) as 8 bf16: gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 widens two e4m3 values (the low or the high
+// 16 bits of a register) straight to two bf16, here with scale 1 (exact).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(const u32x2& w) {
-    const uint32_t w0 = w[0], w1 = w[1];
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
-    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
-    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
     bf16x8 r;
-    r[0] = (__bf16)a[0];
-    r[1] = (__bf16)a[1];
-    r[2] = (__bf16)b[0];
-    r[3] = (__bf16)b[1];
-    r[4] = (__bf16)c[0];
-    r[5] = (__bf16)c[1];
-    r[6] = (__bf16)d[0];
-    r[7] = (__bf16)d[1];
+    r[0] = a[0];
+    r[1] = a[1];
+    r[2] = b[0];
+    r[3] = b[1];
+    r[4] = c[0];
+    r[5] = c[1];
+    r[6] = d[0];
+    r[7] = d[1];
     return r;
 }
 
