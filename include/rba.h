@@ -150,7 +150,7 @@ int rba_prefill(const rba_attn_params* params,
  *                layer's weight layout: element (hp, d, c) multiplies r[..., c]
  *                into the bias at distance d. Head h uses hp = h when
  *                proj_heads == Hq, hp = 0 when proj_heads == 1.
- *   d_r          must be 64 (RBA_ERR_UNSUPPORTED otherwise)
+ *   d_r          32, 64 or 128 (RBA_ERR_UNSUPPORTED otherwise)
  *   proj_heads   1 or Hq (RBA_ERR_SHAPE otherwise)
  *   sink, gate   as rba_prefill_gated (NULL: not applied)
  *   all other arguments as rba_prefill. The bias of distance d is

@@ -360,6 +360,7 @@ int prefill_impl(const rba_attn_params* params, const void* q, const void* k_cac
     a.r = nullptr;
     a.proj = nullptr;
     a.proj_heads = 0;
+    a.d_r = 0;
     a.lscale = o.lscale;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;
@@ -394,7 +395,8 @@ int relproj_impl(const rba_attn_params* params, const void* q, const void* k_cac
     rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
                           max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r", true);
     if (rc || nothing) return rc;
-    if (d_r != 64) return fail(RBA_ERR_UNSUPPORTED, "d_r %d: only 64 is supported", d_r);
+    if (d_r != 32 && d_r != 64 && d_r != 128)
+        return fail(RBA_ERR_UNSUPPORTED, "d_r %d: 32, 64 or 128 are supported", d_r);
     if (proj_heads != 1 && proj_heads != params->num_heads_q)
         return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, params->num_heads_q);
     if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
@@ -407,6 +409,7 @@ int relproj_impl(const rba_attn_params* params, const void* q, const void* k_cac
     a.r = static_cast<const uint16_t*>(r);
     a.proj = static_cast<const uint16_t*>(rel_proj);
     a.proj_heads = proj_heads;
+    a.d_r = d_r;
     a.lscale = o.lscale;
     a.cu_q = cu_q;
     a.seq_lens = seq_lens;

@@ -21,9 +21,10 @@ struct PrefillArgs {
     float* lse;               // fp32 [total_q, Hq] or null
     const float* sink;        // fp32 [total_q, Hq] sink logits, or null (no sink)
     const float* gate;        // fp32 [total_q, Hq] gate logits, or null (no gate)
-    const uint16_t* r;        // bf16 [total_q, Hq, 64] R-branch vectors (bias made in the kernel), or null
-    const uint16_t* proj;     // bf16 [proj_heads, R, 64] rel_logits_proj (linear-weight layout)
+    const uint16_t* r;        // bf16 [total_q, Hq, d_r] R-branch vectors (bias made in the kernel), or null
+    const uint16_t* proj;     // bf16 [proj_heads, R, d_r] rel_logits_proj (linear-weight layout)
     int32_t proj_heads;       // 1 (shared) or Hq
+    int32_t d_r;              // width of r: 32, 64 or 128
     const float* lscale;      // fp32 [total_q] per-row logit scale, or null (1)
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;

@@ -758,14 +758,14 @@ __global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A
 // Prefill with the bias produced in the kernel (rel = r @ rel_logits_proj)
 //
 // Instead of reading rel [rows, Hq, R] from HBM, each wave computes the bias
-// its 32 columns need from r (64 values per column, held as an MFMA operand)
-// and the projection (rows of 64 values per distance, read from L2). The
-// wave's columns are 32 consecutive positions w_lo + n of one head, so for
-// the 32 keys js .. js + 31 of a subtile column n needs the distances
-// (w_lo - js) + n - 31 .. (w_lo - js) + n: 63 distinct distances across the
-// wave, sheared by n. Per subtile the wave computes a band
-// T(js)[rho, n] = r_n . proj[(w_lo - js) - 32 + rho] for rho = 0..31 with four
-// 32x32x16 MFMAs and stores it into a per-column ring of 64 distances that
+// its 32 columns need from r (d_r = 32, 64 or 128 values per column, held as
+// an MFMA operand) and the projection (rows of d_r values per distance, read
+// from L2). The wave's columns are 32 consecutive positions w_lo + n of one
+// head, so for the 32 keys js .. js + 31 of a subtile column n needs the
+// distances (w_lo - js) + n - 31 .. (w_lo - js) + n: 63 distinct distances
+// across the wave, sheared by n. Per subtile the wave computes a band
+// T(js)[rho, n] = r_n . proj[(w_lo - js) - 32 + rho] for rho = 0..31 with
+// d_r / 16 32x32x16 MFMAs and stores it into a per-column ring of 64 distances that
 // also holds T(js - 32) (the distances (w_lo - js) .. + 31). The shear is
 // undone on the way out: each lane reads its 16 bias values as two runs of 8
 // consecutive ring entries starting at a lane-dependent slot. Ring slot of
@@ -777,10 +777,10 @@ __global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A
 // double-buffered whole K/V blocks, so K/V move in half blocks of 64 keys
 // (two subtiles per barrier).
 // ---------------------------------------------------------------------------
-constexpr int DR = 64;       // width of r
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
-template <int DV, bool LS>
+// DR: the width of r (32, 64 or 128).
+template <int DV, bool LS, int DR>
 __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     constexpr int NW = 8;   // every wave issues copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
@@ -1035,14 +1035,14 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
               A.gate ? A.gate[trow] : INFINITY, lane);
 }
 
-template <int DV>
+template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, false>(A);
+    prefill_relproj_body<DV, false, DR>(A);
 }
 
-template <int DV>
+template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_logpos_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, true>(A);
+    prefill_relproj_body<DV, true, DR>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1878,17 +1878,29 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     return hipGetLastError();
 }
 
+namespace {
+
+template <int DV, int DR>
+void launch_relproj_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prefill_relproj_kernel<DV, DR>), g, blk, 0, s, a);
+}
+
+template <int DV>
+void launch_relproj_dv(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.d_r == 32) launch_relproj_t<DV, 32>(a, g, blk, s);
+    else if (a.d_r == 128) launch_relproj_t<DV, 128>(a, g, blk, s);
+    else launch_relproj_t<DV, 64>(a, g, blk, s);
+}
+
+}  // namespace
+
 hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
-    if (a.lscale != nullptr) {  // per-row logit scale
-        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_logpos_kernel<128>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_relproj_logpos_kernel<64>), g, blk, 0, s, a);
-    } else {
-        if (dv == 128) hipLaunchKernelGGL((prefill_relproj_kernel<128>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_relproj_kernel<64>), g, blk, 0, s, a);
-    }
+    if (dv == 128) launch_relproj_dv<128>(a, g, blk, s);
+    else launch_relproj_dv<64>(a, g, blk, s);
     return hipGetLastError();
 }
 

@@ -277,9 +277,9 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
                     logit_scale: Optional[torch.Tensor] = None,
                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill_relproj: as prefill, with the bias made in the kernel from
-    r [total_q, Hq, 64] bf16 and proj [1 or Hq, R, 64] bf16 (rel_logits_proj
-    in linear-weight layout; R = proj.shape[1]). With logit_scale (fp32
-    [total_q]) rba_prefill_relproj_ex runs."""
+    r [total_q, Hq, d_r] bf16 and proj [1 or Hq, R, d_r] bf16 (d_r 32, 64 or
+    128; rel_logits_proj in linear-weight layout; R = proj.shape[1]). With
+    logit_scale (fp32 [total_q]) rba_prefill_relproj_ex runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]

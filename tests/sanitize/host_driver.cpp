@@ -74,7 +74,7 @@ static void prefill_cases() {
                        (const int32_t*)P(), 63, 1, 8192, 8192, (float*)P(), nullptr, nullptr) == RBA_ERR_SHAPE);
     EXPECT(rba_prefill(&p, P(), P(), P(), 64, (const float*)P(), (const int32_t*)P(), (const int32_t*)P(),
                        (const int32_t*)P(), 64, 1, 8192, 0x7fffff00, (float*)P(), nullptr, nullptr) != RBA_OK);
-    EXPECT(rba_prefill_relproj(&p, P(), P(), P(), 64, P(), P(), 32, 1, (const int32_t*)P(), (const int32_t*)P(),
+    EXPECT(rba_prefill_relproj(&p, P(), P(), P(), 64, P(), P(), 48, 1, (const int32_t*)P(), (const int32_t*)P(),
                                (const int32_t*)P(), 64, 1, 100, 8192, nullptr, nullptr, (float*)P(), nullptr,
                                nullptr) == RBA_ERR_UNSUPPORTED);
     EXPECT(rba_prefill_relproj(&p, P(), P(), P(), 64, P(), P(), 64, 3, (const int32_t*)P(), (const int32_t*)P(),

@@ -28,6 +28,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t) {
 
 hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
     expect(a.r && a.proj && (a.proj_heads == 1 || a.proj_heads == a.Hq), "projection");
+    expect(a.d_r == 32 || a.d_r == 64 || a.d_r == 128, "width of r");
     return launch_prefill(a, dv, s);
 }
 

@@ -229,9 +229,10 @@ def test_relproj_prefill_rejects_bad_arguments():
         return lib.rba_prefill_relproj(ctypes.byref(p), q, P, P, 64, r, proj, d_r, heads, P, P, P, 64, batch,
                                        8192, 8192, None, None, out, None, None)
 
-    assert call(d_r=32) == rba.RBA_ERR_UNSUPPORTED
+    assert call(d_r=48) == rba.RBA_ERR_UNSUPPORTED
     assert "d_r" in rba.last_error()
-    assert call(d_r=128) == rba.RBA_ERR_UNSUPPORTED
+    assert call(d_r=16) == rba.RBA_ERR_UNSUPPORTED
+    assert call(d_r=256) == rba.RBA_ERR_UNSUPPORTED
     assert call(heads=3) == rba.RBA_ERR_SHAPE
     assert call(heads=0) == rba.RBA_ERR_SHAPE
     assert call(proj=None) == rba.RBA_ERR_NULL

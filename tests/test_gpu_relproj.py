@@ -66,6 +66,16 @@ def test_relproj_small(case):
     gpu_vs_oracle(b, what=str(case))
 
 
+@pytest.mark.parametrize("d_r", [32, 128])
+@pytest.mark.parametrize("case", [RELPROJ_GRID[i] for i in (0, 1, 2, 3, 7)], ids=_id)
+def test_relproj_other_r_widths(case, d_r):
+    """r of width 32 or 128 (the pages do not give the width of the R branch)."""
+    q_lens, ctx, Hq, Hkv, dv, R, Wn, Hp = case
+    say(f"relproj d_r={d_r} {case}")
+    b = W.make_prefill(24, q_lens, ctx, Hq, Hkv, dv, R, Wn, d_r=d_r, proj_heads=Hp)
+    gpu_vs_oracle(b, what=f"d_r={d_r} {case}")
+
+
 @pytest.mark.parametrize("case", RELPROJ_GRID[:5], ids=_id)
 def test_relproj_equals_materialised_bias(case):
     """The same call through rba_prefill with rel formed by the oracle
@@ -115,10 +125,11 @@ def test_shared_projection_equals_replicated_per_head():
 
 
 def test_relproj_bad_width_is_rejected():
+    """Widths other than 32, 64 and 128 are refused before any launch."""
     b = W.make_prefill(3, [40], [0], 4, 1, 128, 32, 0, d_r=64).to(DEV)
     with pytest.raises(rba.RbaError):
         rba.prefill_relproj(
-            b.q, b.k_cache, b.v_cache, b.r[:, :, :32].contiguous(), b.proj[:, :, :32].contiguous(), b.cu_q,
+            b.q, b.k_cache, b.v_cache, b.r[:, :, :48].contiguous(), b.proj[:, :, :48].contiguous(), b.cu_q,
             b.seq_lens, b.block_tables, window=0, scale=b.scale, max_q_len=40, max_seq_len=40)
 
 
