@@ -369,8 +369,9 @@ int rba_decode_split_fp8(const rba_attn_params* params,
 /*
  * Any combination of the optional terms above in one call: the gated output
  * (sink, gate; rba_prefill_gated / rba_decode_gated), the per-row logit scale
- * (rba_prefill_logpos / rba_decode_logpos) and, for the decode, the e4m3 K/V
- * cache (rba_decode_fp8). Sources: those entry points' sections above. The
+ * (rba_prefill_logpos / rba_decode_logpos) and the e4m3 K/V cache
+ * (rba_decode_fp8; here also for the prefill, whose chunks attend to a cached
+ * context held in FP8). Sources: those entry points' sections above. The
  * terms act at different places, so their composition is fixed: the logit
  * scale multiplies every logit of its row (scale * q.k + bias); the sink is a
  * separate logit that joins the softmax normaliser unscaled; the gate
@@ -383,13 +384,14 @@ typedef struct rba_call_options {
     const float* sink;         /* device fp32 [rows, Hq] or NULL (rows: total_q or batch * n_q)  */
     const float* gate;         /* device fp32 [rows, Hq] or NULL                                  */
     const float* logit_scale;  /* device fp32 [rows] or NULL; finite values                       */
-    int32_t kv_e4m3;           /* 0: bf16 K/V; 1: e4m3 K/V (decode only, RBA_ERR_UNSUPPORTED for  */
-                               /* the prefill); other values RBA_ERR_SHAPE                        */
+    int32_t kv_e4m3;           /* 0: bf16 K/V; 1: e4m3 K/V (prefill and decode; RBA_ERR_UNSUPPORTED */
+                               /* for rba_prefill_relproj_ex); other values RBA_ERR_SHAPE         */
     float k_scale, v_scale;    /* with kv_e4m3 = 1: dequantization scales (finite, > 0)           */
 } rba_call_options;
 
-/* rba_prefill with options (sink, gate, logit_scale). Other arguments and
- * errors as rba_prefill; sink, gate and logit_scale must be 4-byte aligned. */
+/* rba_prefill with options (sink, gate, logit_scale, e4m3 K/V). Other
+ * arguments and errors as rba_prefill (and rba_decode_fp8 for the cache
+ * format and scales); sink, gate and logit_scale must be 4-byte aligned. */
 int rba_prefill_ex(const rba_attn_params* params,
                    const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
                    const float* rel, const int32_t* cu_q, const int32_t* seq_lens,

@@ -11,8 +11,8 @@ namespace rba {
 // One prefill launch: work unit = (sequence, query tile, KV head, head chunk).
 struct PrefillArgs {
     const uint16_t* q;        // bf16 [total_q, Hq, 128]
-    const uint16_t* k;        // bf16 [num_blocks, Hkv, 128, 128]
-    const uint16_t* v;        // bf16 [num_blocks, Hkv, 128, dv]
+    const uint16_t* k;        // bf16 (or e4m3 bytes) [num_blocks, Hkv, 128, 128]
+    const uint16_t* v;        // bf16 (or e4m3 bytes) [num_blocks, Hkv, 128, dv]
     const float* rel;         // fp32 [total_q, Hq, R]
     const int32_t* cu_q;      // [batch + 1]
     const int32_t* seq_lens;  // [batch]
@@ -28,7 +28,9 @@ struct PrefillArgs {
     const float* lscale;      // fp32 [total_q] per-row logit scale, or null (1)
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
-    float c1;                 // scale * log2(e)
+    float c1;                 // scale * log2(e), times the K dequantization scale for e4m3 K/V
+    int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3 (prefill_kernel only)
+    float v_scale;            // V dequantization scale (1 for bf16 K/V)
     int32_t hpw;              // query heads per workgroup (divides G)
     int32_t QT;               // query rows per tile = 32 * (8 / hpw)
     int32_t n_qt;             // query tiles per sequence (from the host max_q_len)

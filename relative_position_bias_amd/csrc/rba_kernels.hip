@@ -366,7 +366,7 @@ __device__ __forceinline__ void init_acc(Cols<DV>& C) {
 // `gate` scales the output by 1 / (1 + e^-gate) (+inf for none).
 template <int DV>
 __device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float* lse, bool bad, float sink,
-                                          float gate, int lane) {
+                                          float gate, int lane, float vscale = 1.f) {
     float l_tot = C.l_sum + xor32(C.l_sum);
     float mref = C.m_ref, o_fac = 1.f;
     if (sink > -INFINITY) {  // move the reference to max(reference, sink) and add the sink's term
@@ -376,7 +376,7 @@ __device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float*
         mref = mn;
     }
     const float g = gate < INFINITY ? 1.f / (1.f + __builtin_amdgcn_exp2f(-gate * LOG2E)) : 1.f;
-    const float inv = bad ? NAN : o_fac / l_tot * g;
+    const float inv = bad ? NAN : o_fac / l_tot * g * vscale;
     const int hh = lane >> 5;
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt) {
@@ -389,6 +389,34 @@ __device__ __forceinline__ void store_out(const Cols<DV>& C, float* orow, float*
         }
     }
     if (lse != nullptr && hh == 0) *lse = bad ? NAN : (mref + __log2f(l_tot)) * LN2;
+}
+
+// e4m3 (OCP FP8) K/V. A cache element is one byte. Every e4m3 value (3
+// mantissa bits, exponents 2^-9 .. 2^8) is exact in bf16, so widening to bf16
+// loses nothing and the MFMAs see exactly the stored values. The
+// dequantization scales are folded into the score scale (K) and the split
+// outputs (V).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 values (lowest address first) as 8 bf16: gfx950's
+// v_cvt_scalef32_pk_bf16_fp8 widens two e4m3 values (the low or the high
+// 16 bits of a register) straight to two bf16, here with scale 1 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(const u32x2& w) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0];
+    r[1] = a[1];
+    r[2] = b[0];
+    r[3] = b[1];
+    r[4] = c[0];
+    r[5] = c[1];
+    r[6] = d[0];
+    r[7] = d[1];
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -479,6 +507,48 @@ __device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* k
 // landed.
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// e4m3 K/V for the prefill: a block's bytes are copied into a staging area
+// in their natural layout (K rows of 128 bytes, then V rows of DV bytes), by
+// the first NW waves, 1 KB per instruction ...
+template <int DV, int NW>
+__device__ __forceinline__ void kv8_dma(uint8_t* S8, const uint8_t* kblk, const uint8_t* vblk, int wid, int lane) {
+    if (wid >= NW) return;
+    constexpr int KI = BS * DQK / 1024, VI = BS * DV / 1024;
+#pragma unroll
+    for (int i = 0; i < (KI + VI + NW - 1) / NW; ++i) {
+        const int grp = wid + NW * i;  // wave-uniform
+        if (grp < KI)
+            dma16(kblk + grp * 1024 + 16 * lane, S8 + grp * 1024);
+        else if (grp < KI + VI)
+            dma16(vblk + (grp - KI) * 1024 + 16 * lane, S8 + grp * 1024);
+    }
+}
+
+// ... and then widened by all 512 threads into the bf16 K/V layouts the
+// readers use (the swizzled K rows and rotated V groups that kv_dma builds);
+// V rows at or past the end of the sequence become zeros.
+template <int DV>
+__device__ __forceinline__ void kv8_widen(__bf16* Ks, __bf16* Vs, const uint8_t* S8, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < BS * DQK / 8 / 512; ++i) {
+        const int u = tid + 512 * i;
+        const int key = u >> 4, c = u & 15;  // key, logical 8-value chunk
+        const u32x2 w = *reinterpret_cast<const u32x2*>(S8 + key * DQK + 8 * c);
+        const int row = (key & ~31) | perm32(key & 31);
+        *reinterpret_cast<bf16x8*>(Ks + row * DQK + 8 * (c ^ (row & 15))) = fp8x8_to_bf16(w);
+    }
+    constexpr int VC = DV / 8;
+#pragma unroll
+    for (int i = 0; i < BS * DV / 8 / 512; ++i) {
+        const int u = tid + 512 * i;
+        const int r = u / VC, c = u % VC;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(S8 + BS * DQK + r * DV + 8 * c);
+        const bf16x8 x = r < nvalid ? fp8x8_to_bf16(w) : fp8x8_to_bf16(u32x2{0u, 0u});
+        const int p = 4 * (((c >> 2) + vrot<DV>(r)) & (DV / 32 - 1)) + (c & 3);
+        *reinterpret_cast<bf16x8*>(Vs + r * DV + 8 * p) = x;
+    }
+}
+
 // S^T for one 32-key subtile of the chunk-swizzled K (koff: the lane's offset
 // of operand st, row (lane & 31), logical chunk 2 st + (lane >> 5)).
 __device__ __forceinline__ f32x16 qk_swz(const __bf16* Ksub, const int (&koff)[8], const bf16x8 (&qreg)[8]) {
@@ -555,13 +625,23 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
 
 // LS: each query row's logits are multiplied by A.lscale[row] (the
 // log-position scale of global layers, "What was built"); otherwise by 1.
-template <int DV, bool WIN, bool LS>
+// KV8: e4m3 K/V caches. Each block is copied as bytes into S8 (the copy of
+// the next block overlaps the current block's compute) and widened into a
+// single pair of bf16 buffers K0 / V0 between two barriers; the compute loop
+// is the bf16 one. The K scale is folded into c1, the V scale into the
+// output.
+template <int DV, bool WIN, bool LS, bool KV8 = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     constexpr int NW = WIN ? 8 : 4;  // waves that issue the K/V copies
     __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 K1[BS * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 ? 8 : BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 V0[BS * DV];
-    __shared__ __attribute__((aligned(16))) __bf16 V1[BS * DV];
+    __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 ? 8 : BS * DV];
+    __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 ? BS * (DQK + DV) : 16];
+    __bf16* const KB = KV8 ? K0 : K1;  // the second buffer pair (the first one again for e4m3)
+    __bf16* const VB = KV8 ? V0 : V1;
+    const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(A.k);
+    const uint8_t* const v8 = reinterpret_cast<const uint8_t*>(A.v);
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
     int id = blockIdx.x;
@@ -662,7 +742,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     bool ok = false;
     {
         const size_t base = block_base(kb_first, ok);
-        if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_first * BS, wid, lane);
+        if constexpr (KV8) {
+            if (ok) kv8_dma<DV, NW>(S8, k8 + base * DQK, v8 + base * DV, wid, lane);
+        } else {
+            if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_first * BS, wid, lane);
+        }
     }
     RelVals rv[2];  // bias of the current and of the next subtile
     if (rel_active(kb_first * BS))
@@ -676,7 +760,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
         const int kbn = kb != kb_last ? next_kb(kb) : -1;  // the next block, if any
-        if (kbn >= 0) {
+        if constexpr (KV8) {
+            kv8_widen<DV>(K0, V0, S8, L - kb * BS, tid);  // this block, bytes -> bf16
+            lds_barrier();                                 // widened block visible, S8 free
+            if (kbn >= 0) {
+                const size_t base = block_base(kbn, ok);
+                if (ok) kv8_dma<DV, NW>(S8, k8 + base * DQK, v8 + base * DV, wid, lane);
+            }
+        } else if (kbn >= 0) {
             const size_t base = block_base(kbn, ok);
             if (ok) kv_dma<DV, NW>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - kbn * BS, wid, lane);
         }
@@ -731,17 +822,17 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
         }
     };
     for (int kb = kb_first;;) {
-        step(K0, V0, K1, V1, kb);
+        step(K0, V0, KB, VB, kb);
         if (kb == kb_last) break;
         kb = next_kb(kb);
-        step(K1, V1, K0, V0, kb);
+        step(KB, VB, K0, V0, kb);
         if (kb == kb_last) break;
         kb = next_kb(kb);
     }
 
     if (!wave_active || !real) return;
     store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
-              A.gate ? A.gate[trow] : INFINITY, lane);
+              A.gate ? A.gate[trow] : INFINITY, lane, KV8 ? A.v_scale : 1.f);
 }
 
 template <int DV, bool WIN>
@@ -752,6 +843,16 @@ __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
 template <int DV, bool WIN>
 __global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A) {
     prefill_body<DV, WIN, true>(A);
+}
+
+template <int DV, bool WIN>
+__global__ void __launch_bounds__(512) prefill_fp8_kernel(const PrefillArgs A) {
+    prefill_body<DV, WIN, false, true>(A);
+}
+
+template <int DV, bool WIN>
+__global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillArgs A) {
+    prefill_body<DV, WIN, true, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1098,34 +1199,6 @@ __device__ __forceinline__ void store_v_sub(__bf16* Vw, const VSub<DV>& v, int l
         const int p = lane + 64 * k;
         *reinterpret_cast<u32x4*>(Vw + (p / (DV / 8)) * vrow<DV>() + 8 * (p % (DV / 8))) = v.r[k];
     }
-}
-
-// e4m3 (OCP FP8) K/V. A cache element is one byte. Every e4m3 value (3
-// mantissa bits, exponents 2^-9 .. 2^8) is exact in bf16, so widening to bf16
-// loses nothing and the MFMAs see exactly the stored values. The
-// dequantization scales are folded into the score scale (K) and the split
-// outputs (V).
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// 8 e4m3 values (lowest address first) as 8 bf16: gfx950's
-// v_cvt_scalef32_pk_bf16_fp8 widens two e4m3 values (the low or the high
-// 16 bits of a register) straight to two bf16, here with scale 1 (exact).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(const u32x2& w) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
-    bf16x8 r;
-    r[0] = a[0];
-    r[1] = a[1];
-    r[2] = b[0];
-    r[3] = b[1];
-    r[4] = c[0];
-    r[5] = c[1];
-    r[6] = d[0];
-    r[7] = d[1];
-    return r;
 }
 
 // load_k_sub for e4m3 K: the same elements, 8 bytes per operand.
@@ -1854,26 +1927,33 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
 
 }  // namespace
 
+namespace {
+
+template <int DV, bool WIN>
+void launch_prefill_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.kv8) {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV, WIN>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_fp8_kernel<DV, WIN>), g, blk, 0, s, a);
+    } else {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_logpos_kernel<DV, WIN>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<DV, WIN>), g, blk, 0, s, a);
+    }
+}
+
+}  // namespace
+
+// Kernel choice: windowed (every subtile streams bias) or not; per-row logit
+// scale or not; bf16 or e4m3 K/V.
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
-    if (a.lscale != nullptr) {  // per-row logit scale
-        if (a.W > 0) {
-            if (dv == 128) hipLaunchKernelGGL((prefill_logpos_kernel<128, true>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((prefill_logpos_kernel<64, true>), g, blk, 0, s, a);
-        } else {
-            if (dv == 128) hipLaunchKernelGGL((prefill_logpos_kernel<128, false>), g, blk, 0, s, a);
-            else hipLaunchKernelGGL((prefill_logpos_kernel<64, false>), g, blk, 0, s, a);
-        }
-        return hipGetLastError();
-    }
-    if (a.W > 0) {  // windowed: every subtile streams bias
-        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<64, true>), g, blk, 0, s, a);
+    if (a.W > 0) {
+        if (dv == 128) launch_prefill_t<128, true>(a, g, blk, s);
+        else launch_prefill_t<64, true>(a, g, blk, s);
     } else {
-        if (dv == 128) hipLaunchKernelGGL((prefill_kernel<128, false>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<64, false>), g, blk, 0, s, a);
+        if (dv == 128) launch_prefill_t<128, false>(a, g, blk, s);
+        else launch_prefill_t<64, false>(a, g, blk, s);
     }
     return hipGetLastError();
 }

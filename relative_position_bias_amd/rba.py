@@ -232,14 +232,15 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
             max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, want_lse: bool = False,
             sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
-            logit_scale: Optional[torch.Tensor] = None,
+            logit_scale: Optional[torch.Tensor] = None, kv_scales: Optional[Tuple[float, float]] = None,
             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill. q [total_q, Hq, 128] bf16; k_cache [nb, Hkv, 128, 128] bf16;
     v_cache [nb, Hkv, 128, dv] bf16; rel [total_q, Hq, R] fp32; cu_q [B+1],
     seq_lens [B], block_tables [B, max_blocks] int32. max_q_len / max_seq_len
     are host-side bounds (no device read happens here). With sink and/or gate
-    (fp32 [total_q, Hq]) and/or logit_scale (fp32 [total_q]), in any
-    combination, rba_prefill_ex runs."""
+    (fp32 [total_q, Hq]), logit_scale (fp32 [total_q]) and/or kv_scales =
+    (k_scale, v_scale) for e4m3 caches (uint8 or torch.float8_e4m3fn), in
+    any combination, rba_prefill_ex runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -255,14 +256,16 @@ def prefill(q, k_cache, v_cache, rel, cu_q, seq_lens, block_tables, *, window: i
     _shape(out, (total_q, Hq, dv), "out")
     _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
-    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
+    kvt = torch.uint8 if kv_scales is not None else torch.bfloat16
+    k_cache, v_cache = (_kv8(k_cache), _kv8(v_cache)) if kv_scales is not None else (k_cache, v_cache)
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, kvt, "k_cache"),
+            _dev(v_cache, kvt, "v_cache"), nb, _dev(rel, torch.float32, "rel"),
             _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
             _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
             int(max_seq_len))
     tail = (_dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
             _stream(stream))
-    opts = call_options(total_q, Hq, sink, gate, logit_scale)
+    opts = call_options(total_q, Hq, sink, gate, logit_scale, kv_scales)
     if opts is None:
         _check(lib().rba_prefill(*args, *tail))
     else:

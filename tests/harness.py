@@ -87,6 +87,8 @@ def oracle_batch(batch: workloads.Batch, rows=None, form="dense"):
 
 
 def run_prefill(b: workloads.Batch, want_lse=False, **kw):
+    if b.kv_fp8:
+        kw.setdefault("kv_scales", (b.k_scale, b.v_scale))
     if b.sink is not None:
         kw.setdefault("sink", b.sink)
     if b.gate is not None:

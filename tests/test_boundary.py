@@ -291,8 +291,9 @@ def test_options_are_checked_before_any_launch():
         return lib.rba_decode_split_ex(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, splits, P,
                                        1 << 30, o, None)
 
-    assert pre(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED      # e4m3 caches: decode only
-    assert rel(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED
+    assert rel(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED      # e4m3 caches: not with the in-kernel bias
+    assert pre(opts(kv_e4m3=1, k_scale=0.0)) == rba.RBA_ERR_SHAPE
+    assert pre(opts(kv_e4m3=1, v_scale=float("inf"))) == rba.RBA_ERR_SHAPE
     assert pre(opts(kv_e4m3=2)) == rba.RBA_ERR_SHAPE
     assert dec(opts(kv_e4m3=-1)) == rba.RBA_ERR_SHAPE
     for field in ("sink", "gate", "logit_scale"):
@@ -305,7 +306,7 @@ def test_options_are_checked_before_any_launch():
     assert "combine" in rba.last_error()
     assert split(opts(gate=P)) == rba.RBA_ERR_UNSUPPORTED
     assert split(None, splits=0) == rba.RBA_ERR_SHAPE             # resolved split count needed
-    assert pre(opts(kv_e4m3=1), batch=0) == rba.RBA_ERR_UNSUPPORTED
+    assert pre(opts(kv_e4m3=1), batch=0) == rba.RBA_OK
     assert pre(opts(sink=P, gate=P, logit_scale=P), batch=0) == rba.RBA_OK   # empty call, no launch
 
 

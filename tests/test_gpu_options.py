@@ -198,3 +198,64 @@ def test_dedicated_decode_entry_points_equal_the_options_call():
     a = split(L.rba_decode_split, head(bf) + mid(bf), ())
     c = split(L.rba_decode_split_ex, head(bf) + mid(bf), (None,))
     assert torch.equal(a, c)
+
+
+# ---------------------------------------------------------------------------
+# prefill over e4m3 K/V caches (chunked prefill of a layer whose cache is FP8)
+# ---------------------------------------------------------------------------
+FP8_PREFILL = [
+    # q_lens, ctx_lens, Hq, Hkv, dv, R, W
+    ([300, 77], [900, 0], 8, 2, 128, 256, 0),
+    ([130], [100], 48, 8, 64, 128, 96),
+    ([257], [300], 12, 2, 128, 512, 160),
+    ([64, 65, 0], [1000, 3, 9], 4, 1, 128, 64, 0),
+    ([200], [4000], 32, 8, 128, 1024, 0),
+]
+
+
+@pytest.mark.parametrize("terms", ["", "gated", "logpos", "gated_logpos"])
+@pytest.mark.parametrize("case", FP8_PREFILL, ids=lambda c: f"q{c[0]}H{c[2]}/{c[3]}dv{c[4]}W{c[6]}")
+def test_prefill_e4m3(case, terms):
+    q_lens, ctx, Hq, Hkv, dv, R, Wn = case
+    say(f"prefill e4m3 {case} {terms}")
+    b = W.make_prefill(67, q_lens, ctx, Hq, Hkv, dv, R, Wn, kv_fp8=True, gated="gated" in terms,
+                       logpos="logpos" in terms)
+    gpu_vs_oracle(b, f"e4m3 {case} {terms}")
+
+
+@pytest.mark.parametrize("Wn", [0, 96])
+def test_prefill_e4m3_equals_bf16_on_dequantized_cache(Wn):
+    """The e4m3 prefill computes the bf16 prefill over caches that hold the
+    dequantised values (exact in bf16 for the workloads' scales). The K scale
+    is a power of two, so folding it into the score scale changes no logit
+    and lse is bitwise equal; the V scale is applied to the output instead of
+    to V, which moves it by fp32 rounding only."""
+    say(f"prefill e4m3 vs bf16 on the dequantized cache, W={Wn}")
+    b8 = W.make_prefill(68, [300, 77], [900, 0], 8, 2, 128, 256, Wn, kv_fp8=True)
+    k = (b8.k_cache.view(torch.float8_e4m3fn).float() * b8.k_scale).to(torch.bfloat16)
+    v = (b8.v_cache.view(torch.float8_e4m3fn).float() * b8.v_scale).to(torch.bfloat16)
+    bb = W.Batch(**{**b8.__dict__, "k_cache": k, "v_cache": v, "kv_fp8": False, "k_scale": 1.0, "v_scale": 1.0})
+    o8, l8 = run_prefill(b8.to(DEV), want_lse=True)
+    ob, lb = run_prefill(bb.to(DEV), want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o8).all()
+    assert torch.equal(l8, lb)
+    assert float((o8 - ob).abs().max()) <= 1e-5
+
+
+def test_prefill_e4m3_32k_chunks_sampled():
+    """The 32K chunked prefill over an e4m3 cache, ~760 sampled rows of each
+    chunk (every 64-row tile, the first and last 256 rows, rows near R)."""
+    from harness import tile_sample_rows
+    name = "global_chunked_prefill_32k_fp8"
+    full = W.build(name)
+    g = full.to(DEV)
+    for c, (ch_gpu, ch_cpu) in enumerate(zip(W.chunks(name, g), W.chunks(name, full))):
+        rows = tile_sample_rows(ch_cpu, seed=c)
+        say(f"{name} chunk {c}: {len(rows)} rows")
+        out, lse = run_prefill(ch_gpu, want_lse=True)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle_batch(ch_cpu, rows=rows)
+        assert_close(out, ref, rows, f"{name} chunk {c}")
+        lmx, _ = errors(lse, ref_lse, rows)
+        assert lmx <= 1e-3, f"chunk {c}: lse max err {lmx:.3e}"

@@ -67,6 +67,7 @@ WORKLOADS["local_prefill_8k_relproj"] = dict(WORKLOADS["local_prefill_8k"], d_r=
 WORKLOADS["global_chunked_prefill_32k_relproj"] = dict(WORKLOADS["global_chunked_prefill_32k"], d_r=64)
 # Global-layer calls with a per-row log-position logit scale.
 WORKLOADS["global_chunked_prefill_32k_logpos"] = dict(WORKLOADS["global_chunked_prefill_32k"], logpos=True)
+WORKLOADS["global_chunked_prefill_32k_fp8"] = dict(WORKLOADS["global_chunked_prefill_32k"], kv_fp8=True)
 WORKLOADS["paged_decode_16x8k_128k_disjoint_logpos"] = dict(WORKLOADS["paged_decode_16x8k_128k_disjoint"],
                                                           logpos=True)
 # The decode workloads again over e4m3 K/V caches.
@@ -182,13 +183,15 @@ def _tables_tensor(tables: List[List[int]], max_blocks: int) -> torch.Tensor:
 def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv: int, dv: int, R: int,
                  W: int, permute: bool = True, scale: Optional[float] = None,
                  extra_blocks: int = 0, gated: bool = False, d_r: int = 0, proj_heads: int = 1,
-                 logpos: bool = False) -> Batch:
+                 logpos: bool = False, kv_fp8: bool = False) -> Batch:
     """Sequences with ctx_lens[b] cached tokens followed by q_lens[b] new ones
     (whose K/V are already in the cache). One pool holds every sequence's
     blocks, disjoint, permuted if `permute`. With d_r > 0 the bias is given
     by its producer instead: r ~ N(0, 1) [rows, Hq, d_r] and a projection
     ~ N(0, 0.25 / d_r) [proj_heads, R, d_r], so that rel = r @ proj^T has the
-    N(0, 0.5^2) entries of the materialised workloads; rel is then None."""
+    N(0, 0.5^2) entries of the materialised workloads; rel is then None.
+    With kv_fp8 the caches are converted to e4m3 bytes after every draw
+    (as in make_decode)."""
     gen = torch.Generator().manual_seed(seed)
     seq_lens = [c + q for c, q in zip(ctx_lens, q_lens)]
     nblk = [(L + BLOCK - 1) // BLOCK for L in seq_lens]
@@ -214,6 +217,10 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
     extra = _gated(total_q, Hq, gen) if gated else {}
     if logpos:
         extra["lscale"] = _logpos(total_q, gen)
+    if kv_fp8:
+        k_cache = _to_e4m3(k_cache, K_SCALE_FP8)
+        v_cache = _to_e4m3(v_cache, V_SCALE_FP8)
+        extra.update(kv_fp8=True, k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
     cu = [0]
     for ql in q_lens:
         cu.append(cu[-1] + ql)
@@ -292,7 +299,8 @@ def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
                  sink=full.sink[a:b] if full.sink is not None else None,
                  gate=full.gate[a:b] if full.gate is not None else None,
                  r=full.r[a:b] if full.r is not None else None, proj=full.proj,
-                 lscale=full.lscale[a:b] if full.lscale is not None else None)
+                 lscale=full.lscale[a:b] if full.lscale is not None else None,
+                 kv_fp8=full.kv_fp8, k_scale=full.k_scale, v_scale=full.v_scale)
 
 
 def build(name: str, seed: int = 0) -> Batch:
@@ -306,7 +314,8 @@ def build(name: str, seed: int = 0) -> Batch:
         total = w.pop("total")
         w.pop("chunk")
         return make_prefill(seed, [total], [0], w["Hq"], w["Hkv"], w["dv"], w["R"], w["W"],
-                            d_r=w.get("d_r", 0), proj_heads=w.get("proj_heads", 1), logpos=w.get("logpos", False))
+                            d_r=w.get("d_r", 0), proj_heads=w.get("proj_heads", 1), logpos=w.get("logpos", False),
+                            kv_fp8=w.get("kv_fp8", False))
     return make_decode(seed, **w)
 
 
