@@ -69,10 +69,11 @@ def test_relproj_any_rel_extent(R):
 # ---------------------------------------------------------------------------
 # device lengths outside the contract: NaN rows, other sequences unchanged
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
 @pytest.mark.parametrize("bad_len", ["past_table", "short_of_rows"])
-def test_prefill_bad_device_length_gives_nan_rows(bad_len):
-    say(f"prefill bad length {bad_len}")
-    b = W.make_prefill(56, [100, 50], [200, 0], 8, 2, 128, 128, 0).to(DEV)
+def test_prefill_bad_device_length_gives_nan_rows(bad_len, fp8):
+    say(f"prefill bad length {bad_len} fp8={fp8}")
+    b = W.make_prefill(56, [100, 50], [200, 0], 8, 2, 128, 128, 0, kv_fp8=fp8).to(DEV)
     ref, _ = run_prefill(b)
     maxb = b.block_tables.shape[1]
     bad = W.Batch(**{**b.__dict__})
@@ -135,12 +136,13 @@ def untouched(full, n):
     return bool((g == CANARY).all())
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
 @pytest.mark.parametrize("case", [([300, 77], [900, 0], 8, 2, 128, 256, 0), ([130], [100], 48, 8, 64, 128, 96)],
                          ids=["nowin", "win_dv64"])
-def test_prefill_writes_only_out_and_lse(case):
+def test_prefill_writes_only_out_and_lse(case, fp8):
     q_lens, ctx, Hq, Hkv, dv, R, Wn = case
-    say(f"guard bands prefill {case}")
-    b = W.make_prefill(58, q_lens, ctx, Hq, Hkv, dv, R, Wn).to(DEV)
+    say(f"guard bands prefill {case} fp8={fp8}")
+    b = W.make_prefill(58, q_lens, ctx, Hq, Hkv, dv, R, Wn, kv_fp8=fp8).to(DEV)
     fo, out = guarded(b.rows * Hq * dv)
     fl, lse = guarded(b.rows * Hq)
     run_prefill(b, out=out.view(b.rows, Hq, dv), lse=lse.view(b.rows, Hq))
