@@ -58,6 +58,23 @@ static void prefill_cases() {
                     EXPECT(rba_prefill_relproj(&p, P(), P(), P(), 64, P(), P(), 64, 1, (const int32_t*)P(),
                                                (const int32_t*)P(), (const int32_t*)P(), 64, 1, 100, 8192, nullptr,
                                                nullptr, (float*)P(), nullptr, nullptr) == RBA_OK);
+                    for (int mask = 0; mask < 16; ++mask) {  // every mix of sink, gate, logit scale, e4m3
+                        rba_call_options o;
+                        memset(&o, 0, sizeof(o));
+                        o.sink = (mask & 1) ? (const float*)P(4) : nullptr;
+                        o.gate = (mask & 2) ? (const float*)P(8) : nullptr;
+                        o.logit_scale = (mask & 4) ? (const float*)P(12) : nullptr;
+                        o.kv_e4m3 = (mask & 8) ? 1 : 0;
+                        o.k_scale = 0.5f;
+                        o.v_scale = 0.25f;
+                        EXPECT(rba_prefill_ex(&p, P(), P(), P(), 64, rel, (const int32_t*)P(), (const int32_t*)P(),
+                                              (const int32_t*)P(), 64, 2, 300, 8192, &o, (float*)P(), (float*)P(4),
+                                              nullptr) == RBA_OK);
+                        const int want = (mask & 8) ? RBA_ERR_UNSUPPORTED : RBA_OK;
+                        EXPECT(rba_prefill_relproj_ex(&p, P(), P(), P(), 64, P(), P(), 32 << (mask & 2 ? 1 : 0), 1,
+                                                      (const int32_t*)P(), (const int32_t*)P(), (const int32_t*)P(),
+                                                      64, 1, 100, 8192, &o, (float*)P(), nullptr, nullptr) == want);
+                    }
                 }
     rba_attn_params p = prm(32, 8, 128, 512, 512);
     // rejected arguments: nothing launched, an error code and a message
@@ -83,6 +100,25 @@ static void prefill_cases() {
     EXPECT(rba_prefill_logpos(&p, P(), P(), P(), 64, (const float*)P(), (const int32_t*)P(), (const int32_t*)P(),
                               (const int32_t*)P(), 64, 1, 100, 8192, nullptr, (float*)P(), nullptr,
                               nullptr) == RBA_ERR_NULL);
+    {  // options checked before anything else
+        rba_call_options o;
+        memset(&o, 0, sizeof(o));
+        o.kv_e4m3 = 2;
+        EXPECT(rba_prefill_ex(&p, P(), P(), P(), 64, (const float*)P(), (const int32_t*)P(), (const int32_t*)P(),
+                              (const int32_t*)P(), 64, 1, 8192, 8192, &o, (float*)P(), nullptr, nullptr) ==
+               RBA_ERR_SHAPE);
+        o.kv_e4m3 = 1;
+        o.k_scale = 0.f;
+        o.v_scale = 1.f;
+        EXPECT(rba_prefill_ex(&p, P(), P(), P(), 64, (const float*)P(), (const int32_t*)P(), (const int32_t*)P(),
+                              (const int32_t*)P(), 64, 1, 8192, 8192, &o, (float*)P(), nullptr, nullptr) ==
+               RBA_ERR_SHAPE);
+        o.kv_e4m3 = 0;
+        o.sink = (const float*)P(2);
+        EXPECT(rba_prefill_ex(&p, P(), P(), P(), 64, (const float*)P(), (const int32_t*)P(), (const int32_t*)P(),
+                              (const int32_t*)P(), 64, 1, 8192, 8192, &o, (float*)P(), nullptr, nullptr) ==
+               RBA_ERR_UNSUPPORTED);
+    }
     // empty calls need no pointers
     EXPECT(rba_prefill(&p, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, nullptr,
                        nullptr, nullptr) == RBA_OK);
@@ -121,6 +157,19 @@ static void decode_cases() {
                         EXPECT(rba_decode_logpos(&p, P(), P(), P(), maxb, (const float*)P(4), (const int32_t*)P(),
                                                  (const int32_t*)P(), maxb, 3, n_q, msl, 0, P(), ws,
                                                  (const float*)P(4), (float*)P(), nullptr, nullptr) == RBA_OK);
+                        for (int mask = 0; mask < 16; ++mask) {
+                            rba_call_options o;
+                            memset(&o, 0, sizeof(o));
+                            o.sink = (mask & 1) ? (const float*)P(4) : nullptr;
+                            o.gate = (mask & 2) ? (const float*)P(8) : nullptr;
+                            o.logit_scale = (mask & 4) ? (const float*)P(12) : nullptr;
+                            o.kv_e4m3 = (mask & 8) ? 1 : 0;
+                            o.k_scale = 0.5f;
+                            o.v_scale = 0.25f;
+                            EXPECT(rba_decode_ex(&p, P(), P(), P(), maxb, (const float*)P(4), (const int32_t*)P(),
+                                                 (const int32_t*)P(), maxb, 3, n_q, msl, 0, P(), ws, &o, (float*)P(),
+                                                 nullptr, nullptr) == RBA_OK);
+                        }
                         const size_t ws3 = rba_decode_workspace_size(&p, 3, n_q, msl, 3);
                         EXPECT(rba_decode_split(&p, P(), P(), P(), maxb, (const float*)P(4), (const int32_t*)P(),
                                                 (const int32_t*)P(), maxb, 3, n_q, msl, 3, P(), ws3,
@@ -143,6 +192,23 @@ static void decode_cases() {
                           (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), 1 << 30, (float*)P(), nullptr,
                           nullptr) == RBA_ERR_SHAPE);
     EXPECT(rba_decode_combine(&p, 1, 1, 0, P(), 1 << 30, (float*)P(), nullptr, nullptr) == RBA_ERR_SHAPE);
+    {  // the split stage alone takes no sink or gate, and needs a resolved split count
+        rba_call_options o;
+        memset(&o, 0, sizeof(o));
+        o.sink = (const float*)P(4);
+        EXPECT(rba_decode_split_ex(&p, P(), P(), P(), 8, (const float*)P(), (const int32_t*)P(),
+                                   (const int32_t*)P(), 8, 1, 1, 1000, 2, P(), 1 << 30, &o, nullptr) ==
+               RBA_ERR_UNSUPPORTED);
+        o.sink = nullptr;
+        o.kv_e4m3 = 1;
+        o.k_scale = o.v_scale = 1.f;
+        o.logit_scale = (const float*)P(4);
+        EXPECT(rba_decode_split_ex(&p, P(), P(), P(), 8, (const float*)P(), (const int32_t*)P(),
+                                   (const int32_t*)P(), 8, 1, 1, 1000, 2, P(), 1 << 30, &o, nullptr) == RBA_OK);
+        EXPECT(rba_decode_split_ex(&p, P(), P(), P(), 8, (const float*)P(), (const int32_t*)P(),
+                                   (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), 1 << 30, &o, nullptr) ==
+               RBA_ERR_SHAPE);
+    }
 }
 
 int main() {
