@@ -384,8 +384,8 @@ typedef struct rba_call_options {
     const float* sink;         /* device fp32 [rows, Hq] or NULL (rows: total_q or batch * n_q)  */
     const float* gate;         /* device fp32 [rows, Hq] or NULL                                  */
     const float* logit_scale;  /* device fp32 [rows] or NULL; finite values                       */
-    int32_t kv_e4m3;           /* 0: bf16 K/V; 1: e4m3 K/V (prefill and decode; RBA_ERR_UNSUPPORTED */
-                               /* for rba_prefill_relproj_ex); other values RBA_ERR_SHAPE         */
+    int32_t kv_e4m3;           /* 0: bf16 K/V; 1: e4m3 K/V (every entry point taking options);    */
+                               /* other values RBA_ERR_SHAPE                                      */
     float k_scale, v_scale;    /* with kv_e4m3 = 1: dequantization scales (finite, > 0)           */
 } rba_call_options;
 
@@ -399,9 +399,9 @@ int rba_prefill_ex(const rba_attn_params* params,
                    int32_t batch, int32_t max_q_len, int32_t max_seq_len,
                    const rba_call_options* options, float* out, float* lse, void* stream);
 
-/* rba_prefill_relproj with options (sink, gate, logit_scale; the scale also
- * multiplies the bias made in the kernel). Other arguments and errors as
- * rba_prefill_relproj. */
+/* rba_prefill_relproj with options (sink, gate, logit_scale, e4m3 K/V; the
+ * logit scale also multiplies the bias made in the kernel). Other arguments
+ * and errors as rba_prefill_relproj. */
 int rba_prefill_relproj_ex(const rba_attn_params* params,
                            const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
                            const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,

@@ -320,13 +320,11 @@ int check_opts(const Opts& o) {
     return o.kv8 ? check_kv_scales(o.k_scale, o.v_scale) : RBA_OK;
 }
 
-int read_options(const rba_call_options* in, bool e4m3_ok, Opts* o) {
+int read_options(const rba_call_options* in, Opts* o) {
     *o = Opts();
     if (in == nullptr) return RBA_OK;
     if (in->kv_e4m3 != 0 && in->kv_e4m3 != 1)
         return fail(RBA_ERR_SHAPE, "kv_e4m3 %d must be 0 or 1", in->kv_e4m3);
-    if (in->kv_e4m3 && !e4m3_ok)
-        return fail(RBA_ERR_UNSUPPORTED, "e4m3 K/V caches are not supported by the in-kernel-bias prefill");
     o->sink = in->sink;
     o->gate = in->gate;
     o->lscale = in->logit_scale;
@@ -429,9 +427,9 @@ int relproj_impl(const rba_attn_params* params, const void* q, const void* k_cac
     a.G = params->num_heads_q / params->num_heads_kv;
     a.R = params->rel_extent;
     a.W = params->window;
-    a.c1 = (float)((double)params->scale * 1.4426950408889634);
-    a.kv8 = 0;
-    a.v_scale = 1.f;
+    a.c1 = (float)((double)params->scale * (o.kv8 ? (double)o.k_scale : 1.0) * 1.4426950408889634);
+    a.kv8 = o.kv8 ? 1 : 0;
+    a.v_scale = o.kv8 ? o.v_scale : 1.f;
     tile_shape(a, max_q_len);
     hipError_t e = rba::launch_prefill_relproj(a, params->head_dim_v, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -504,7 +502,7 @@ int rba_prefill_ex(const rba_attn_params* params, const void* q, const void* k_c
                    const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len,
                    int32_t max_seq_len, const rba_call_options* options, float* out, float* lse, void* stream) {
     Opts o;
-    int rc = read_options(options, true, &o);
+    int rc = read_options(options, &o);
     if (rc) return rc;
     return prefill_impl(params, q, k_cache, v_cache, num_blocks, rel, cu_q, seq_lens, block_tables,
                         max_blocks_per_seq, batch, max_q_len, max_seq_len, o, out, lse, stream);
@@ -544,7 +542,7 @@ int rba_prefill_relproj_ex(const rba_attn_params* params, const void* q, const v
                            int32_t max_blocks_per_seq, int32_t batch, int32_t max_q_len, int32_t max_seq_len,
                            const rba_call_options* options, float* out, float* lse, void* stream) {
     Opts o;
-    int rc = read_options(options, false, &o);
+    int rc = read_options(options, &o);
     if (rc) return rc;
     return relproj_impl(params, q, k_cache, v_cache, num_blocks, r, rel_proj, d_r, proj_heads, cu_q, seq_lens,
                         block_tables, max_blocks_per_seq, batch, max_q_len, max_seq_len, o, out, lse, stream);
@@ -610,7 +608,7 @@ int rba_decode_split_ex(const rba_attn_params* params, const void* q, const void
                         int32_t num_splits, void* workspace, size_t workspace_bytes, const rba_call_options* options,
                         void* stream) {
     Opts o;
-    int rc = read_options(options, true, &o);
+    int rc = read_options(options, &o);
     if (rc) return rc;
     return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
                        batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, o, false, false, nullptr,
@@ -670,7 +668,7 @@ int rba_decode_ex(const rba_attn_params* params, const void* q, const void* k_ca
                   void* workspace, size_t workspace_bytes, const rba_call_options* options, float* out, float* lse,
                   void* stream) {
     Opts o;
-    int rc = read_options(options, true, &o);
+    int rc = read_options(options, &o);
     if (rc) return rc;
     return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
                        batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, o, true, false, out, lse,

@@ -507,13 +507,14 @@ __device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* k
 // landed.
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// e4m3 K/V for the prefill: a block's bytes are copied into a staging area
-// in their natural layout (K rows of 128 bytes, then V rows of DV bytes), by
-// the first NW waves, 1 KB per instruction ...
-template <int DV, int NW>
+// e4m3 K/V for the prefill: the bytes of ROWS keys (a block or half of one)
+// are copied into a staging area in their natural layout (K rows of 128
+// bytes, then V rows of DV bytes), by the first NW waves, 1 KB per
+// instruction ...
+template <int DV, int NW, int ROWS = BS>
 __device__ __forceinline__ void kv8_dma(uint8_t* S8, const uint8_t* kblk, const uint8_t* vblk, int wid, int lane) {
     if (wid >= NW) return;
-    constexpr int KI = BS * DQK / 1024, VI = BS * DV / 1024;
+    constexpr int KI = ROWS * DQK / 1024, VI = ROWS * DV / 1024;
 #pragma unroll
     for (int i = 0; i < (KI + VI + NW - 1) / NW; ++i) {
         const int grp = wid + NW * i;  // wave-uniform
@@ -527,10 +528,10 @@ __device__ __forceinline__ void kv8_dma(uint8_t* S8, const uint8_t* kblk, const 
 // ... and then widened by all 512 threads into the bf16 K/V layouts the
 // readers use (the swizzled K rows and rotated V groups that kv_dma builds);
 // V rows at or past the end of the sequence become zeros.
-template <int DV>
+template <int DV, int ROWS = BS>
 __device__ __forceinline__ void kv8_widen(__bf16* Ks, __bf16* Vs, const uint8_t* S8, int nvalid, int tid) {
 #pragma unroll
-    for (int i = 0; i < BS * DQK / 8 / 512; ++i) {
+    for (int i = 0; i < ROWS * DQK / 8 / 512; ++i) {
         const int u = tid + 512 * i;
         const int key = u >> 4, c = u & 15;  // key, logical 8-value chunk
         const u32x2 w = *reinterpret_cast<const u32x2*>(S8 + key * DQK + 8 * c);
@@ -539,10 +540,10 @@ __device__ __forceinline__ void kv8_widen(__bf16* Ks, __bf16* Vs, const uint8_t*
     }
     constexpr int VC = DV / 8;
 #pragma unroll
-    for (int i = 0; i < BS * DV / 8 / 512; ++i) {
+    for (int i = 0; i < ROWS * DV / 8 / 512; ++i) {
         const int u = tid + 512 * i;
         const int r = u / VC, c = u % VC;
-        const u32x2 w = *reinterpret_cast<const u32x2*>(S8 + BS * DQK + r * DV + 8 * c);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(S8 + ROWS * DQK + r * DV + 8 * c);
         const bf16x8 x = r < nvalid ? fp8x8_to_bf16(w) : fp8x8_to_bf16(u32x2{0u, 0u});
         const int p = 4 * (((c >> 2) + vrot<DV>(r)) & (DV / 32 - 1)) + (c & 3);
         *reinterpret_cast<bf16x8*>(Vs + r * DV + 8 * p) = x;
@@ -880,17 +881,23 @@ __global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillAr
 // ---------------------------------------------------------------------------
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
-// DR: the width of r (32, 64 or 128).
-template <int DV, bool LS, int DR>
+// DR: the width of r (32, 64 or 128). KV8: e4m3 K/V caches, staged and
+// widened per stage as in prefill_body (one pair of bf16 stage buffers).
+template <int DV, bool LS, int DR, bool KV8 = false>
 __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     constexpr int NW = 8;   // every wave issues copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
     __shared__ __attribute__((aligned(16))) __bf16 K0[HB * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 K1[HB * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 ? 8 : HB * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 V0[HB * DV];
-    __shared__ __attribute__((aligned(16))) __bf16 V1[HB * DV];
+    __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 ? 8 : HB * DV];
+    __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 ? HB * (DQK + DV) : 16];
     __shared__ __attribute__((aligned(16))) float ring_all[8 * 32 * RSTRIDE];
+    __bf16* const KB = KV8 ? K0 : K1;
+    __bf16* const VB = KV8 ? V0 : V1;
+    const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(A.k);
+    const uint8_t* const v8 = reinterpret_cast<const uint8_t*>(A.v);
 
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
     const int hh = lane >> 5;
@@ -1065,7 +1072,11 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     bool ok = false;
     {
         const size_t row = stage_row(s_lo, ok);
-        if (ok) kv_dma<DV, NW, HB>(K0, V0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
+        if constexpr (KV8) {
+            if (ok) kv8_dma<DV, NW, HB>(S8, k8 + row * DQK, v8 + row * DV, wid, lane);
+        } else {
+            if (ok) kv_dma<DV, NW, HB>(K0, V0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
+        }
     }
     int band_js = INT_MIN;  // last band in the ring
     int pv_js = INT_MIN;    // band whose projection rows pv holds
@@ -1084,6 +1095,10 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
         const int js0 = s * HB, js1 = js0 + 32;
+        if constexpr (KV8) {
+            kv8_widen<DV, HB>(K0, V0, S8, L - js0, tid);  // this stage, bytes -> bf16
+            lds_barrier();                                 // widened stage visible, S8 free
+        }
         const bool comp0 = wave_active && ok_cur && !masked_all(C, js0, A.W);
         const bool comp1 = wave_active && ok_cur && !masked_all(C, js1, A.W);
         const bool bias0 = comp0 && bias_on(C, js0, A.R);
@@ -1100,7 +1115,11 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
         }
         if (s < s_hi) {
             const size_t row = stage_row(s + 1, ok);
-            if (ok) kv_dma<DV, NW, HB>(Kn, Vn, A.k + row * DQK, A.v + row * DV, L - (s + 1) * HB, wid, lane);
+            if constexpr (KV8) {
+                if (ok) kv8_dma<DV, NW, HB>(S8, k8 + row * DQK, v8 + row * DV, wid, lane);
+            } else {
+                if (ok) kv_dma<DV, NW, HB>(Kn, Vn, A.k + row * DQK, A.v + row * DV, L - (s + 1) * HB, wid, lane);
+            }
         }
         if (bias1 && band_js == js0) {
             load_p(pv, js1);
@@ -1125,15 +1144,15 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
         if (comp1) compute(Kc, Vc, 1, js1, bias1);
     };
     for (int s = s_lo;;) {
-        step(K0, V0, K1, V1, s);
+        step(K0, V0, KB, VB, s);
         if (++s > s_hi) break;
-        step(K1, V1, K0, V0, s);
+        step(KB, VB, K0, V0, s);
         if (++s > s_hi) break;
     }
 
     if (!wave_active || !real) return;
     store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
-              A.gate ? A.gate[trow] : INFINITY, lane);
+              A.gate ? A.gate[trow] : INFINITY, lane, KV8 ? A.v_scale : 1.f);
 }
 
 template <int DV, int DR>
@@ -1144,6 +1163,16 @@ __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs 
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_logpos_kernel(const PrefillArgs A) {
     prefill_relproj_body<DV, true, DR>(A);
+}
+
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_fp8_kernel(const PrefillArgs A) {
+    prefill_relproj_body<DV, false, DR, true>(A);
+}
+
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_fp8_logpos_kernel(const PrefillArgs A) {
+    prefill_relproj_body<DV, true, DR, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -1962,8 +1991,13 @@ namespace {
 
 template <int DV, int DR>
 void launch_relproj_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_logpos_kernel<DV, DR>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((prefill_relproj_kernel<DV, DR>), g, blk, 0, s, a);
+    if (a.kv8) {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_fp8_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_fp8_kernel<DV, DR>), g, blk, 0, s, a);
+    } else {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_kernel<DV, DR>), g, blk, 0, s, a);
+    }
 }
 
 template <int DV>

@@ -277,12 +277,13 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
                     max_q_len: int, max_seq_len: int, out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, want_lse: bool = False,
                     sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
-                    logit_scale: Optional[torch.Tensor] = None,
+                    logit_scale: Optional[torch.Tensor] = None, kv_scales: Optional[Tuple[float, float]] = None,
                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """rba_prefill_relproj: as prefill, with the bias made in the kernel from
     r [total_q, Hq, d_r] bf16 and proj [1 or Hq, R, d_r] bf16 (d_r 32, 64 or
     128; rel_logits_proj in linear-weight layout; R = proj.shape[1]). With
-    logit_scale (fp32 [total_q]) rba_prefill_relproj_ex runs."""
+    logit_scale (fp32 [total_q]) and/or kv_scales (e4m3 caches)
+    rba_prefill_relproj_ex runs."""
     total_q, Hq, dqk = q.shape
     nb, Hkv, bs, _ = k_cache.shape
     dv = v_cache.shape[3]
@@ -301,19 +302,21 @@ def prefill_relproj(q, k_cache, v_cache, r, proj, cu_q, seq_lens, block_tables, 
     _shape(out, (total_q, Hq, dv), "out")
     _shape(lse, (total_q, Hq), "lse")
     p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
-    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
-            _dev(v_cache, torch.bfloat16, "v_cache"), nb, _dev(r, torch.bfloat16, "r"),
+    kvt = torch.uint8 if kv_scales is not None else torch.bfloat16
+    k_cache, v_cache = (_kv8(k_cache), _kv8(v_cache)) if kv_scales is not None else (k_cache, v_cache)
+    args = (ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k_cache, kvt, "k_cache"),
+            _dev(v_cache, kvt, "v_cache"), nb, _dev(r, torch.bfloat16, "r"),
             _dev(proj, torch.bfloat16, "proj"), d_r, proj_heads,
             _dev(cu_q, torch.int32, "cu_q"), _dev(seq_lens, torch.int32, "seq_lens"),
             _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1], batch, int(max_q_len),
             int(max_seq_len))
     tail = (_dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse") if lse is not None else None,
             _stream(stream))
-    if logit_scale is None:
+    if logit_scale is None and kv_scales is None:
         _check(lib().rba_prefill_relproj(*args, _opt(sink, "sink", (total_q, Hq)), _opt(gate, "gate", (total_q, Hq)),
                                          *tail))
     else:
-        opts = call_options(total_q, Hq, sink, gate, logit_scale)
+        opts = call_options(total_q, Hq, sink, gate, logit_scale, kv_scales)
         _check(lib().rba_prefill_relproj_ex(*args, ctypes.byref(opts), *tail))
     return out, lse
 

@@ -70,10 +70,9 @@ static void prefill_cases() {
                         EXPECT(rba_prefill_ex(&p, P(), P(), P(), 64, rel, (const int32_t*)P(), (const int32_t*)P(),
                                               (const int32_t*)P(), 64, 2, 300, 8192, &o, (float*)P(), (float*)P(4),
                                               nullptr) == RBA_OK);
-                        const int want = (mask & 8) ? RBA_ERR_UNSUPPORTED : RBA_OK;
                         EXPECT(rba_prefill_relproj_ex(&p, P(), P(), P(), 64, P(), P(), 32 << (mask & 2 ? 1 : 0), 1,
                                                       (const int32_t*)P(), (const int32_t*)P(), (const int32_t*)P(),
-                                                      64, 1, 100, 8192, &o, (float*)P(), nullptr, nullptr) == want);
+                                                      64, 1, 100, 8192, &o, (float*)P(), nullptr, nullptr) == RBA_OK);
                     }
                 }
     rba_attn_params p = prm(32, 8, 128, 512, 512);

@@ -23,7 +23,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t) {
     expect(a.Hq == a.Hkv * a.G && a.G % a.hpw == 0 && a.n_hc * a.hpw == a.G, "head split");
     expect(a.QT == 32 * (8 / a.hpw) && a.n_qt >= 1 && a.batch >= 1, "tiles");
     expect(a.R >= 1 && a.W >= 0 && a.max_blocks >= 1 && a.num_blocks >= 1, "sizes");
-    expect((a.kv8 == 0 && a.v_scale == 1.f) || (a.kv8 == 1 && a.v_scale > 0.f && a.r == nullptr), "K/V type");
+    expect((a.kv8 == 0 && a.v_scale == 1.f) || (a.kv8 == 1 && a.v_scale > 0.f), "K/V type");
     return hipSuccess;
 }
 

@@ -291,7 +291,7 @@ def test_options_are_checked_before_any_launch():
         return lib.rba_decode_split_ex(ctypes.byref(d), P, P, P, 2560, P, P, P, 1024, 16, 1, 131072, splits, P,
                                        1 << 30, o, None)
 
-    assert rel(opts(kv_e4m3=1)) == rba.RBA_ERR_UNSUPPORTED      # e4m3 caches: not with the in-kernel bias
+    assert rel(opts(kv_e4m3=1, k_scale=-1.0)) == rba.RBA_ERR_SHAPE
     assert pre(opts(kv_e4m3=1, k_scale=0.0)) == rba.RBA_ERR_SHAPE
     assert pre(opts(kv_e4m3=1, v_scale=float("inf"))) == rba.RBA_ERR_SHAPE
     assert pre(opts(kv_e4m3=2)) == rba.RBA_ERR_SHAPE

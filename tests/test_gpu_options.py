@@ -259,3 +259,18 @@ def test_prefill_e4m3_32k_chunks_sampled():
         assert_close(out, ref, rows, f"{name} chunk {c}")
         lmx, _ = errors(lse, ref_lse, rows)
         assert lmx <= 1e-3, f"chunk {c}: lse max err {lmx:.3e}"
+
+
+@pytest.mark.parametrize("terms", ["", "gated_logpos"])
+@pytest.mark.parametrize("case", [([200, 90], [700, 0], 8, 2, 128, 300, 0, 1, 64),
+                                  ([150], [400], 8, 2, 64, 256, 160, 8, 32),
+                                  ([130], [1000], 16, 2, 128, 1024, 0, 1, 128)],
+                         ids=["nowin_shared", "win_perhead_dr32", "g8_dr128"])
+def test_relproj_e4m3(case, terms):
+    """The in-kernel-bias prefill over e4m3 caches (each half-block stage
+    staged as bytes and widened to bf16)."""
+    q_lens, ctx, Hq, Hkv, dv, R, Wn, ph, d_r = case
+    say(f"relproj e4m3 {case} {terms}")
+    b = W.make_prefill(69, q_lens, ctx, Hq, Hkv, dv, R, Wn, d_r=d_r, proj_heads=ph, kv_fp8=True,
+                       gated="gated" in terms, logpos="logpos" in terms)
+    gpu_vs_oracle(b, f"relproj e4m3 {case} {terms}")

@@ -40,7 +40,7 @@ def prefill_case(seed):
     opts = dict(gated=rnd.random() < 0.25, logpos=rnd.random() < 0.25)
     if rnd.random() < 0.25:
         opts.update(d_r=rnd.choice([32, 64, 128]), proj_heads=rnd.choice([1, Hq]))
-    if rnd.random() < 0.25 and "d_r" not in opts:   # e4m3 caches (not with the in-kernel bias)
+    if rnd.random() < 0.25:   # e4m3 caches
         opts.update(kv_fp8=True)
     return (q_lens, ctx, Hq, Hkv, dv, R, Wn), opts
 
