@@ -46,10 +46,16 @@
 //   * Prefill with the bias made in the kernel (rel = r @ rel_logits_proj,
 //     "Attention with a relative bias"): each wave forms the 63-distance band
 //     of a subtile from r (an MFMA operand held for the whole sweep) and the
-//     projection rows (from L2) with four more MFMAs, keeps the last two
+//     projection rows (from L2) with d_r / 16 more MFMAs, keeps the last two
 //     32-distance bands in a per-column LDS ring, and reads each lane's
 //     values back along the shear. The ring leaves room for half-block K/V
 //     stages only.
+//   * e4m3 (FP8) K/V caches ("vLLM TML Inkling Support", "Future Roadmap"):
+//     the decode widens each piece to bf16 in registers as it is loaded; the
+//     prefill copies a block's (or stage's) bytes into a staging area of LDS
+//     and widens them there, between two barriers, into the bf16 layouts its
+//     compute loop reads. K's scale folds into the score scale, V's into the
+//     output.
 //   * Decode: each of the 4 waves of a workgroup streams its own 32-key
 //     subtile of every block of the split without any barrier: K goes straight
 //     from HBM into MFMA operand registers, V into a wave-private LDS tile.
