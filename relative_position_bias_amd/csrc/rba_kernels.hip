@@ -357,6 +357,14 @@ __device__ __forceinline__ void load_q(Cols<DV>& C, const uint16_t* qrow, int la
     for (int st = 0; st < 8; ++st) C.qreg[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hh);
 }
 
+// load_q in the dimension order of load_k_sub8 (e4m3 K)
+template <int DV>
+__device__ __forceinline__ void load_q8(Cols<DV>& C, const uint16_t* qrow, int lane) {
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) C.qreg[st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * (st >> 1) + 16 * hh + 8 * (st & 1));
+}
+
 template <int DV>
 __device__ __forceinline__ void init_acc(Cols<DV>& C) {
 #pragma unroll
@@ -1236,11 +1244,17 @@ __device__ __forceinline__ void store_v_sub(__bf16* Vw, const VSub<DV>& v, int l
     }
 }
 
-// load_k_sub for e4m3 K: the same elements, 8 bytes per operand.
+// load_k_sub for e4m3 K, with the head dimension taken in another order (the
+// same for q, see load_q8) so that one 16-byte load feeds two score MFMAs:
+// step st of lane half hh covers dims 32 (st >> 1) + 16 hh + 8 (st & 1) .. +8.
 __device__ __forceinline__ void load_k_sub8(u32x2 (&kr)[8], const uint8_t* kblk, int sub, int lane) {
-    const uint8_t* row = kblk + (32 * sub + perm32(lane & 31)) * DQK + 8 * (lane >> 5);
+    const uint8_t* row = kblk + (32 * sub + perm32(lane & 31)) * DQK + 16 * (lane >> 5);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) kr[st] = *reinterpret_cast<const u32x2*>(row + 16 * st);
+    for (int s2 = 0; s2 < 4; ++s2) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(row + 32 * s2);
+        kr[2 * s2] = u32x2{w[0], w[1]};
+        kr[2 * s2 + 1] = u32x2{w[2], w[3]};
+    }
 }
 
 // V subtile of e4m3 V as 16-byte pieces of 16 values; widened to bf16 when
@@ -1359,7 +1373,10 @@ __device__ __forceinline__ void decode_split_body(const DecodeArgs A) {
     C.w_lo = L - A.n_q + (cg * 32) / A.G;
     C.w_hi = L - A.n_q + c_hi / A.G;
     C.phantom = c_hi < cg * 32 + 31;
-    load_q(C, A.q + trow * DQK, lane);
+    if constexpr (KV8)
+        load_q8(C, A.q + trow * DQK, lane);
+    else
+        load_q(C, A.q + trow * DQK, lane);
     init_acc(C);
 
     const int nb = L / BS + (L % BS != 0);
@@ -1593,13 +1610,22 @@ __device__ __forceinline__ float groups_sum(float v) {
 
 // K operands of one 32-key subtile: kr[2 h + ... ] in order (h, s):
 // lane loads key 32 sub + 8 (m/4) + 4 h + m%4 (m = l & 15), dims 32 s + 8 q.
+// e4m3 K: the head dimension is taken in a different order (the same for q,
+// see dims16_e4m3) so that each 16-byte load feeds two score MFMAs: step st
+// of lane group q covers dims 16 (q + 4 (st >> 1)) + 8 (st & 1) + 0..7.
+__device__ __forceinline__ int dims16_e4m3(int st, int q) { return 16 * (q + 4 * (st >> 1)) + 8 * (st & 1); }
+
 __device__ __forceinline__ void load_k16(u32x2 (&kr)[8], const uint8_t* kblk, int sub, int lane) {
     const int m = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint8_t* row = kblk + (32 * sub + 8 * (m >> 2) + 4 * h + (m & 3)) * DQK + 8 * q;
+        const uint8_t* row = kblk + (32 * sub + 8 * (m >> 2) + 4 * h + (m & 3)) * DQK;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) kr[4 * h + st] = *reinterpret_cast<const u32x2*>(row + 32 * st);
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(row + dims16_e4m3(2 * s2, q));
+            kr[4 * h + 2 * s2] = u32x2{w[0], w[1]};
+            kr[4 * h + 2 * s2 + 1] = u32x2{w[2], w[3]};
+        }
     }
 }
 
@@ -1674,9 +1700,11 @@ __device__ __forceinline__ void decode16_split_body(const DecodeArgs A) {
     const bool phantom = ncols < 16;
 
     bf16x8 qreg[4];
-    // as load_q: a column past the last real one reads a real row
+    // as load_q: a column past the last real one reads a real row (over
+    // e4m3 K/V in the dimension order of load_k16)
 #pragma unroll
-    for (int st = 0; st < 4; ++st) qreg[st] = *reinterpret_cast<const bf16x8*>(A.q + trow * DQK + 32 * st + 8 * q);
+    for (int st = 0; st < 4; ++st)
+        qreg[st] = *reinterpret_cast<const bf16x8*>(A.q + trow * DQK + (KV8 ? dims16_e4m3(st, q) : 32 * st + 8 * q));
     f32x4v O[DV / 16];
 #pragma unroll
     for (int t = 0; t < DV / 16; ++t) O[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
