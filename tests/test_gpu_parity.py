@@ -422,6 +422,22 @@ def test_repeatable_bitwise():
         assert torch.equal(run_prefill(p)[0], pref)
 
 
+def test_repeatable_bitwise_e4m3():
+    """The same over e4m3 K/V caches: 50 runs of a decode (16- and 32-column
+    kernels) and of a prefill are bitwise identical."""
+    say("repeatability, e4m3")
+    for n_q in (1, 4):
+        b = W.make_decode(3, 3, n_q, 32, 8, 128, 1024, 0, seq_lens=[7000, 260, 2100], kv_fp8=True).to(DEV)
+        ref, _ = run_decode(b)
+        for _ in range(50):
+            o, _ = run_decode(b)
+            assert torch.equal(o, ref), f"decode n_q={n_q}"
+    p = W.make_prefill(3, [300, 77], [900, 0], 8, 2, 128, 512, 0, kv_fp8=True).to(DEV)
+    pref, _ = run_prefill(p)
+    for _ in range(50):
+        assert torch.equal(run_prefill(p)[0], pref)
+
+
 def test_graph_capture_replay():
     say("graph capture")
     b = W.make_decode(13, 2, 4, 64, 8, 64, 1024, 0, seq_lens=[2000, 5000]).to(DEV)
@@ -444,6 +460,37 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
         run_prefill(W.make_prefill(1, [64], [0], 4, 1, 128, 128, 0).to(DEV))   # eager work between
+
+
+def test_graph_capture_replay_e4m3():
+    """A decode and a prefill over e4m3 caches captured in one graph: every
+    replay, with eager work between them, reproduces the eager outputs."""
+    say("graph capture, e4m3")
+    b = W.make_decode(14, 2, 1, 32, 8, 128, 1024, 0, seq_lens=[3000, 9000], kv_fp8=True).to(DEV)
+    p = W.make_prefill(14, [200, 64], [500, 1000], 8, 2, 128, 256, 0, kv_fp8=True).to(DEV)
+    ws = torch.empty(rba.workspace_size(32, 8, 128, 1024, 0, b.scale, 2, 1, b.max_seq_len), dtype=torch.uint8,
+                     device=DEV)
+    out_d = torch.empty((2, 32, 128), device=DEV)
+    out_p = torch.empty((p.rows, p.Hq, p.dv), device=DEV)
+    eager_d = run_decode(b, workspace=ws)[0].clone()
+    eager_p = run_prefill(p)[0].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_decode(b, workspace=ws, out=out_d)
+        run_prefill(p, out=out_p)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_decode(b, workspace=ws, out=out_d)
+        run_prefill(p, out=out_p)
+    for _ in range(3):
+        out_d.fill_(7.0)
+        out_p.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d, eager_d) and torch.equal(out_p, eager_p)
+        run_decode(W.make_decode(1, 1, 1, 32, 8, 128, 1024, 0, seq_lens=[500], kv_fp8=True).to(DEV))
 
 
 @pytest.mark.parametrize("shape", [(1, 8, 2, 128), (4, 64, 8, 64)], ids=["4col_dv128", "32col_dv64"])
