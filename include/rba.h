@@ -432,6 +432,44 @@ int rba_decode_split_ex(const rba_attn_params* params,
                         void* stream);
 
 /*
+ * Decode with the bias made from the R branch instead of a materialised rel.
+ * Source: "Inkling-Small on Gaudi 2", section "Attention with a relative
+ * bias" (each layer forms rel as r times its rel_logits_proj and hands it to
+ * the attention call); the same reading as rba_prefill_relproj (one r vector
+ * of width d_r per token and query head; one projection shared by the heads
+ * or one per head). A decode step's bias covers only its batch * n_q query
+ * rows, batch * n_q * Hq * R floats, small next to the cached context the
+ * step reads; so the call first forms those rows with a small kernel, into
+ * the workspace, and then runs the rba_decode kernels on them.
+ *
+ *   r            device bf16 [batch * n_q, Hq, d_r], rows as q
+ *   rel_proj     device bf16 [proj_heads, R, d_r], as rba_prefill_relproj
+ *   d_r          32, 64 or 128 (RBA_ERR_UNSUPPORTED otherwise)
+ *   proj_heads   1 or Hq (RBA_ERR_SHAPE otherwise)
+ *   workspace    device memory of at least
+ *                rba_decode_relproj_workspace_size(...) bytes, 16-byte
+ *                aligned: the split partials as for rba_decode, then, from the
+ *                next multiple of 256 bytes, the bias rows fp32
+ *                [batch * n_q, Hq, R]. Its contents on entry are ignored.
+ *   options      as rba_decode_ex (NULL: none)
+ *   all other arguments as rba_decode. The bias of distance d is
+ *   sum_c r[t, h, c] * rel_proj[hp, d, c] (exact products, fp32 sum in
+ *   the order of c) for 0 <= d < R and 0 beyond. r and rel_proj must be
+ *   16-byte aligned.
+ * Errors: as rba_decode_ex; every check runs before the first launch.
+ */
+size_t rba_decode_relproj_workspace_size(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                                         int32_t max_seq_len, int32_t num_splits);
+
+int rba_decode_relproj(const rba_attn_params* params,
+                       const void* q, const void* k_cache, const void* v_cache, int32_t num_blocks,
+                       const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                       const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits,
+                       void* workspace, size_t workspace_bytes, const rba_call_options* options,
+                       float* out, float* lse, void* stream);
+
+/*
  * rba_decode without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). The split partials go to a scratch array that the

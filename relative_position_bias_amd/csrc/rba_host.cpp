@@ -158,6 +158,27 @@ size_t ws_bytes(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t sp
     return pairs * (size_t)splits * ((size_t)p->head_dim_v + 1) * sizeof(float);
 }
 
+// rba_decode_relproj's workspace: the split partials (ws_bytes), then, from
+// the next multiple of 256 bytes, the bias rows fp32 [batch*n_q, Hq, R].
+size_t rel_rows_offset(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_t splits) {
+    return (ws_bytes(p, batch, n_q, splits) + 255) / 256 * 256;
+}
+
+size_t rel_rows_bytes(const rba_attn_params* p, int32_t batch, int32_t n_q) {
+    return (size_t)batch * n_q * p->num_heads_q * (size_t)p->rel_extent * sizeof(float);
+}
+
+int check_producer(const rba_attn_params* p, const void* r, const void* rel_proj, int32_t d_r,
+                   int32_t proj_heads) {
+    if (d_r != 32 && d_r != 64 && d_r != 128)
+        return fail(RBA_ERR_UNSUPPORTED, "d_r %d: 32, 64 or 128 are supported", d_r);
+    if (proj_heads != 1 && proj_heads != p->num_heads_q)
+        return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, p->num_heads_q);
+    if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
+    if (!aligned16(r) || !aligned16(rel_proj)) return fail(RBA_ERR_UNSUPPORTED, "r/rel_proj must be 16-byte aligned");
+    return RBA_OK;
+}
+
 // `rel` is the bias source the call reads (rel, or r for the in-kernel
 // producer), named `rel_name` in messages.
 int validate_prefill(const rba_attn_params* p, const void* q, const void* k_cache, const void* v_cache,
@@ -201,7 +222,7 @@ int validate_decode(const rba_attn_params* p, const void* q, const void* k_cache
                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
                     int32_t max_seq_len, int32_t num_splits, const void* workspace,
                     size_t workspace_bytes, const float* out, const float* lse, bool need_out,
-                    int32_t* splits_out, bool* nothing) {
+                    int32_t* splits_out, bool* nothing, const char* rel_name = "rel") {
     *nothing = false;
     int rc = check_params(p);
     if (rc) return rc;
@@ -213,13 +234,14 @@ int validate_decode(const rba_attn_params* p, const void* q, const void* k_cache
         *nothing = true;
         return ok();
     }
-    if (q == nullptr || rel == nullptr || seq_lens == nullptr) return fail(RBA_ERR_NULL, "q/rel/seq_lens is NULL");
+    if (q == nullptr || rel == nullptr || seq_lens == nullptr)
+        return fail(RBA_ERR_NULL, "q/%s/seq_lens is NULL", rel_name);
     if (need_out && out == nullptr) return fail(RBA_ERR_NULL, "out is NULL");
     rc = check_cache(k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, max_seq_len);
     if (rc) return rc;
     if (!aligned16(q) || (need_out && !aligned16(out)))
         return fail(RBA_ERR_UNSUPPORTED, "q/out must be 16-byte aligned");
-    if (!aligned4(rel)) return fail(RBA_ERR_UNSUPPORTED, "rel must be 4-byte aligned");
+    if (!aligned4(rel)) return fail(RBA_ERR_UNSUPPORTED, "%s must be 4-byte aligned", rel_name);
     if (!aligned4(seq_lens) || (lse != nullptr && !aligned4(lse)))
         return fail(RBA_ERR_UNSUPPORTED, "seq_lens/lse must be 4-byte aligned");
     const int32_t splits = num_splits ? num_splits : plan_splits(p, batch, n_q, max_seq_len, device_cus());
@@ -396,12 +418,8 @@ int relproj_impl(const rba_attn_params* params, const void* q, const void* k_cac
     rc = validate_prefill(params, q, k_cache, v_cache, num_blocks, r, cu_q, seq_lens, block_tables,
                           max_blocks_per_seq, batch, max_q_len, max_seq_len, out, lse, &nothing, "r", true);
     if (rc || nothing) return rc;
-    if (d_r != 32 && d_r != 64 && d_r != 128)
-        return fail(RBA_ERR_UNSUPPORTED, "d_r %d: 32, 64 or 128 are supported", d_r);
-    if (proj_heads != 1 && proj_heads != params->num_heads_q)
-        return fail(RBA_ERR_SHAPE, "proj_heads %d must be 1 or Hq %d", proj_heads, params->num_heads_q);
-    if (rel_proj == nullptr) return fail(RBA_ERR_NULL, "rel_proj is NULL");
-    if (!aligned16(rel_proj)) return fail(RBA_ERR_UNSUPPORTED, "rel_proj must be 16-byte aligned");
+    rc = check_producer(params, r, rel_proj, d_r, proj_heads);
+    if (rc) return rc;
     rba::PrefillArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k_cache);
@@ -580,6 +598,16 @@ size_t rba_decode_workspace_size(const rba_attn_params* params, int32_t batch, i
     return ws_bytes(params, batch, n_q, splits);
 }
 
+size_t rba_decode_relproj_workspace_size(const rba_attn_params* params, int32_t batch, int32_t n_q,
+                                         int32_t max_seq_len, int32_t num_splits) {
+    if (check_params(params)) return 0;
+    if (check_decode_shape(params, batch, n_q, max_seq_len)) return 0;
+    if (num_splits < 0 || num_splits > 1024) return 0;
+    if (batch == 0) return 0;
+    const int32_t splits = num_splits ? num_splits : plan_splits(params, batch, n_q, max_seq_len, device_cus());
+    return rel_rows_offset(params, batch, n_q, splits) + rel_rows_bytes(params, batch, n_q);
+}
+
 int rba_validate_decode(const rba_attn_params* params, const void* q, const void* k_cache,
                         const void* v_cache, int32_t num_blocks, const float* rel, const int32_t* seq_lens,
                         const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t batch, int32_t n_q,
@@ -741,6 +769,57 @@ int rba_decode_fp8(const rba_attn_params* params, const void* q, const void* k_c
     return decode_impl(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables, max_blocks_per_seq,
                        batch, n_q, max_seq_len, num_splits, workspace, workspace_bytes, fp8_opts(k_scale, v_scale),
                        true, false, out, lse, stream, "rba_decode_fp8");
+}
+
+int rba_decode_relproj(const rba_attn_params* params, const void* q, const void* k_cache, const void* v_cache,
+                       int32_t num_blocks, const void* r, const void* rel_proj, int32_t d_r, int32_t proj_heads,
+                       const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       int32_t batch, int32_t n_q, int32_t max_seq_len, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes, const rba_call_options* options, float* out, float* lse,
+                       void* stream) {
+    // Every check (the decode's own included) runs before the first launch.
+    Opts o;
+    int rc = read_options(options, &o);
+    if (rc) return rc;
+    rc = check_opts(o);
+    if (rc) return rc;
+    bool nothing;
+    int32_t splits = 0;
+    rc = validate_decode(params, q, k_cache, v_cache, num_blocks, static_cast<const float*>(r), seq_lens,
+                         block_tables, max_blocks_per_seq, batch, n_q, max_seq_len, num_splits, workspace,
+                         workspace_bytes, out, lse, true, &splits, &nothing, "r");
+    if (rc || nothing) return rc;
+    rc = check_producer(params, r, rel_proj, d_r, proj_heads);
+    if (rc) return rc;
+    const size_t off = rel_rows_offset(params, batch, n_q, splits);
+    const size_t need = off + rel_rows_bytes(params, batch, n_q);
+    if (workspace_bytes < need)
+        return fail(RBA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if ((int64_t)params->rel_extent * params->num_heads_q * batch * n_q > ((int64_t)1 << 40))
+        return fail(RBA_ERR_UNSUPPORTED, "bias rows too large");
+    rba::RelRowsArgs ra;
+    ra.r = static_cast<const uint16_t*>(r);
+    ra.proj = static_cast<const uint16_t*>(rel_proj);
+    ra.rel = reinterpret_cast<float*>(static_cast<char*>(workspace) + off);
+    ra.rows = batch * n_q;
+    ra.Hq = params->num_heads_q;
+    ra.R = params->rel_extent;
+    ra.d_r = d_r;
+    ra.proj_heads = proj_heads;
+    // rows per workgroup: the fewest (a power of two) that keep the grid
+    // within about three workgroups per CU, and the grid's z extent legal
+    {
+        const int64_t xy = ceil_div(ra.R, 256) * (int64_t)ra.Hq;
+        int64_t rpw = 1;
+        while (rpw < ra.rows && (xy * ceil_div(ra.rows, rpw) > 3LL * device_cus() || ceil_div(ra.rows, rpw) > 65535))
+            rpw *= 2;
+        ra.rows_per_wg = (int32_t)rpw;
+    }
+    hipError_t e = rba::launch_rel_rows(ra, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "bias rows launch");
+    return decode_impl(params, q, k_cache, v_cache, num_blocks, ra.rel, seq_lens, block_tables, max_blocks_per_seq,
+                       batch, n_q, max_seq_len, splits, workspace, workspace_bytes, o, true, false, out, lse, stream,
+                       "rba_decode_relproj");
 }
 
 }  // extern "C"

@@ -68,10 +68,22 @@ struct CombineArgs {
     int32_t splits;
 };
 
+// Bias rows of a decode step from the R branch:
+// rel[row, h, d] = sum_c r[row, h, c] * proj[hp, d, c], hp = 0 or h.
+struct RelRowsArgs {
+    const uint16_t* r;        // bf16 [rows, Hq, d_r]
+    const uint16_t* proj;     // bf16 [proj_heads, R, d_r] (linear-weight layout)
+    float* rel;               // fp32 [rows, Hq, R]
+    int32_t rows, Hq, R;
+    int32_t d_r;              // 32, 64 or 128
+    int32_t proj_heads;       // 1 (shared) or Hq
+    int32_t rows_per_wg;      // rows of one workgroup (grid z = ceil(rows / rows_per_wg) <= 65535)
+};
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s);
 hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s);
+hipError_t launch_rel_rows(const RelRowsArgs& a, hipStream_t s);
 
 // The device scratch of rba_decode_noalloc: a file-scope device array of
 // RBA_NOALLOC_SCRATCH_BYTES bytes in the kernels' code object, one copy per

@@ -1988,6 +1988,64 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs A) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Bias rows of a decode step made from the R branch ("Inkling-Small on Gaudi
+// 2", "Attention with a relative bias": rel = r @ rel_logits_proj), written
+// as fp32 [rows, Hq, R] for the decode kernels to read. A decode step's bias
+// is rows * Hq * R floats, small next to the context it attends to, so it is
+// formed by this separate small kernel rather than inside the split kernel.
+// One workgroup per (256 distances, query head h, group of A.rows_per_wg
+// rows; the host sizes the groups so that about one round of workgroups fills
+// the GPU); lane j of wave w keeps the projection row of distance
+// d0 + 64 w + j (as fp32) in registers. The group's r vectors of head h are
+// staged in LDS, 64 rows at a time, and read back as broadcasts. Each bias is
+// the sum over the components c, in order, of r[row, h, c] * proj[hp, d, c]:
+// exact products, fp32 accumulation.
+// ---------------------------------------------------------------------------
+constexpr int RR_ROWS = 64;  // r rows per LDS stage
+
+template <int DR>
+__global__ void __launch_bounds__(256) rel_rows_kernel(const RelRowsArgs A) {
+    __shared__ __attribute__((aligned(16))) uint16_t rs[RR_ROWS * DR];
+    const int tid = threadIdx.x;
+    const int h = blockIdx.y;
+    const int d = blockIdx.x * 256 + tid;
+    const bool live = d < A.R;
+    const int hp = A.proj_heads == 1 ? 0 : h;
+    // a lane past the last distance reads distance R - 1 and stores nothing
+    const uint16_t* prow = A.proj + ((size_t)hp * A.R + (live ? d : A.R - 1)) * DR;
+    float pf[DR];
+#pragma unroll
+    for (int c8 = 0; c8 < DR / 8; ++c8) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(prow + 8 * c8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pf[8 * c8 + i] = (float)v[i];
+    }
+    const int g0 = blockIdx.z * A.rows_per_wg, g1 = min(A.rows, g0 + A.rows_per_wg);
+#pragma unroll 1
+    for (int r0 = g0; r0 < g1; r0 += RR_ROWS) {
+        const int nr = min(RR_ROWS, g1 - r0);
+        __syncthreads();  // the previous stage's readers are done
+        for (int p = tid; p < nr * (DR / 8); p += 256) {
+            const int row = r0 + p / (DR / 8), c8 = p % (DR / 8);
+            *reinterpret_cast<bf16x8*>(rs + (p / (DR / 8)) * DR + 8 * c8) =
+                *reinterpret_cast<const bf16x8*>(A.r + ((size_t)row * A.Hq + h) * DR + 8 * c8);
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int k = 0; k < nr; ++k) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c8 = 0; c8 < DR / 8; ++c8) {
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(rs + k * DR + 8 * c8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc = fmaf((float)v[i], pf[8 * c8 + i], acc);
+            }
+            if (live) A.rel[((size_t)(r0 + k) * A.Hq + h) * A.R + d] = acc;
+        }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -2123,6 +2181,18 @@ hipError_t noalloc_scratch(void** ptr) {
     }
     *ptr = p;
     return hipSuccess;
+}
+
+hipError_t launch_rel_rows(const RelRowsArgs& a, hipStream_t s) {
+    if (a.rows <= 0 || a.Hq <= 0 || a.R <= 0) return hipSuccess;
+    if (a.rows_per_wg < 1) return hipErrorInvalidValue;
+    const dim3 g((unsigned)((a.R + 255) / 256), (unsigned)a.Hq, (unsigned)((a.rows + a.rows_per_wg - 1) / a.rows_per_wg));
+    const dim3 blk(256);
+    if (a.d_r == 32) hipLaunchKernelGGL(rel_rows_kernel<32>, g, blk, 0, s, a);
+    else if (a.d_r == 64) hipLaunchKernelGGL(rel_rows_kernel<64>, g, blk, 0, s, a);
+    else if (a.d_r == 128) hipLaunchKernelGGL(rel_rows_kernel<128>, g, blk, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t s) {

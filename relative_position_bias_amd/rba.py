@@ -112,6 +112,10 @@ _SIGNATURES = {
     "rba_decode_split_ex": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _ptr,
                                            _i32, _i32, _i32, _i32, _i32, _ptr, _size,
                                            ctypes.POINTER(CallOptions), _ptr]),
+    "rba_decode_relproj_workspace_size": (_size, [ctypes.POINTER(AttnParams), _i32, _i32, _i32, _i32]),
+    "rba_decode_relproj": (ctypes.c_int, [ctypes.POINTER(AttnParams), _ptr, _ptr, _ptr, _i32, _ptr, _ptr, _i32,
+                                          _i32, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _ptr, _size,
+                                          ctypes.POINTER(CallOptions), _ptr, _ptr, _ptr]),
 }
 
 NOALLOC_SCRATCH_BYTES = 16 << 20   # RBA_NOALLOC_SCRATCH_BYTES in include/rba.h
@@ -398,6 +402,62 @@ def decode(q, k_cache, v_cache, rel, seq_lens, block_tables, *, n_q: int, window
         _check(L.rba_decode(*args, *tail))
     else:
         _check(L.rba_decode_ex(*args, ctypes.byref(opts), *tail))
+    return out, lse
+
+
+def relproj_workspace_size(Hq, Hkv, dv, rel_extent, window, scale, batch, n_q, max_seq_len, num_splits=0) -> int:
+    p = params(Hq, Hkv, dv, rel_extent, window, scale)
+    return lib().rba_decode_relproj_workspace_size(ctypes.byref(p), batch, n_q, max_seq_len, num_splits)
+
+
+def decode_relproj(q, k_cache, v_cache, r, proj, seq_lens, block_tables, *, n_q: int, window: int,
+                   scale: float, max_seq_len: int, num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   want_lse: bool = False, kv_scales: Optional[Tuple[float, float]] = None,
+                   sink: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+                   logit_scale: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """rba_decode_relproj: as decode, with the bias rows made by the library
+    from r [batch*n_q, Hq, d_r] bf16 and proj [1 or Hq, R, d_r] bf16 (d_r 32,
+    64 or 128; R = proj.shape[1]). `workspace` (uint8) holds the split
+    partials and the bias rows; allocated with torch if not given."""
+    rows, Hq, dqk = q.shape
+    if r.dim() != 3 or r.shape[:2] != (rows, Hq):
+        raise ValueError("r must be [batch * n_q, Hq, d_r]")
+    d_r = r.shape[2]
+    if proj.dim() != 3 or proj.shape[2] != d_r:
+        raise ValueError("proj must be [proj_heads, R, d_r]")
+    proj_heads, R = proj.shape[0], proj.shape[1]
+    nb, Hkv, bs, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    if rows % n_q != 0:
+        raise ValueError("q rows must be batch * n_q")
+    batch = rows // n_q
+    if seq_lens.numel() != batch:
+        raise ValueError("seq_lens must have batch entries")
+    _cache_shapes(q, k_cache, v_cache, block_tables, batch)
+    p = params(Hq, Hkv, dv, R, window, scale, dqk, bs)
+    L = lib()
+    need = L.rba_decode_relproj_workspace_size(ctypes.byref(p), batch, n_q, int(max_seq_len), int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((rows, Hq, dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    _shape(out, (rows, Hq, dv), "out")
+    _shape(lse, (rows, Hq), "lse")
+    k8 = _kv8(k_cache) if kv_scales is not None else k_cache
+    v8 = _kv8(v_cache) if kv_scales is not None else v_cache
+    kvt = torch.uint8 if kv_scales is not None else torch.bfloat16
+    opts = call_options(rows, Hq, sink, gate, logit_scale, kv_scales)
+    _check(L.rba_decode_relproj(
+        ctypes.byref(p), _dev(q, torch.bfloat16, "q"), _dev(k8, kvt, "k_cache"), _dev(v8, kvt, "v_cache"), nb,
+        _dev(r, torch.bfloat16, "r"), _dev(proj, torch.bfloat16, "proj"), d_r, proj_heads,
+        _dev(seq_lens, torch.int32, "seq_lens"), _dev(block_tables, torch.int32, "block_tables"),
+        block_tables.shape[1], batch, n_q, int(max_seq_len), int(num_splits), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), ctypes.byref(opts) if opts is not None else None, _dev(out, torch.float32, "out"),
+        _dev(lse, torch.float32, "lse") if lse is not None else None, _stream(stream)))
     return out, lse
 
 

@@ -113,6 +113,10 @@ def run_decode(b: workloads.Batch, num_splits=0, want_lse=False, **kw):
         kw.setdefault("gate", b.gate)
     if b.lscale is not None:
         kw.setdefault("logit_scale", b.lscale)
+    if b.r is not None:
+        return rba.decode_relproj(b.q, b.k_cache, b.v_cache, b.r, b.proj, b.seq_lens, b.block_tables, n_q=b.n_q,
+                                  window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
+                                  want_lse=want_lse, **kw)
     return rba.decode(b.q, b.k_cache, b.v_cache, b.rel, b.seq_lens, b.block_tables, n_q=b.n_q,
                       window=b.W, scale=b.scale, max_seq_len=b.max_seq_len, num_splits=num_splits,
                       want_lse=want_lse, **kw)

@@ -169,6 +169,19 @@ static void decode_cases() {
                                                  (const int32_t*)P(), maxb, 3, n_q, msl, 0, P(), ws, &o, (float*)P(),
                                                  nullptr, nullptr) == RBA_OK);
                         }
+                        // bias rows made from r: the workspace adds them after the partials
+                        const size_t wr = rba_decode_relproj_workspace_size(&p, 3, n_q, msl, 0);
+                        EXPECT(wr >= ws + (size_t)3 * n_q * p.num_heads_q * p.rel_extent * 4);
+                        for (int d_r : {32, 64, 128})
+                            for (int ph : {1, p.num_heads_q}) {
+                                EXPECT(rba_decode_relproj(&p, P(), P(), P(), maxb, P(), P(), d_r, ph,
+                                                          (const int32_t*)P(), (const int32_t*)P(), maxb, 3, n_q,
+                                                          msl, 0, P(), wr, nullptr, (float*)P(), nullptr,
+                                                          nullptr) == RBA_OK);
+                            }
+                        EXPECT(rba_decode_relproj(&p, P(), P(), P(), maxb, P(), P(), 64, 1, (const int32_t*)P(),
+                                                  (const int32_t*)P(), maxb, 3, n_q, msl, 0, P(), wr - 1, nullptr,
+                                                  (float*)P(), nullptr, nullptr) == RBA_ERR_WORKSPACE);
                         const size_t ws3 = rba_decode_workspace_size(&p, 3, n_q, msl, 3);
                         EXPECT(rba_decode_split(&p, P(), P(), P(), maxb, (const float*)P(4), (const int32_t*)P(),
                                                 (const int32_t*)P(), maxb, 3, n_q, msl, 3, P(), ws3,
@@ -191,6 +204,35 @@ static void decode_cases() {
                           (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), 1 << 30, (float*)P(), nullptr,
                           nullptr) == RBA_ERR_SHAPE);
     EXPECT(rba_decode_combine(&p, 1, 1, 0, P(), 1 << 30, (float*)P(), nullptr, nullptr) == RBA_ERR_SHAPE);
+    {  // the bias made from r: argument checks
+        const size_t wr = rba_decode_relproj_workspace_size(&p, 1, 1, 1000, 0);
+        EXPECT(wr > rba_decode_workspace_size(&p, 1, 1, 1000, 0));
+        EXPECT(rba_decode_relproj_workspace_size(&p, 1, 0, 1000, 0) == 0);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(), P(), 48, 1, (const int32_t*)P(), (const int32_t*)P(),
+                                  8, 1, 1, 1000, 0, P(), wr, nullptr, (float*)P(), nullptr, nullptr) ==
+               RBA_ERR_UNSUPPORTED);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(), P(), 64, 3, (const int32_t*)P(), (const int32_t*)P(),
+                                  8, 1, 1, 1000, 0, P(), wr, nullptr, (float*)P(), nullptr, nullptr) ==
+               RBA_ERR_SHAPE);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, nullptr, P(), 64, 1, (const int32_t*)P(),
+                                  (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), wr, nullptr, (float*)P(), nullptr,
+                                  nullptr) == RBA_ERR_NULL);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(), nullptr, 64, 1, (const int32_t*)P(),
+                                  (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), wr, nullptr, (float*)P(), nullptr,
+                                  nullptr) == RBA_ERR_NULL);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(8), P(), 64, 1, (const int32_t*)P(),
+                                  (const int32_t*)P(), 8, 1, 1, 1000, 0, P(), wr, nullptr, (float*)P(), nullptr,
+                                  nullptr) == RBA_ERR_UNSUPPORTED);
+        rba_call_options o;
+        memset(&o, 0, sizeof(o));
+        o.kv_e4m3 = 1;
+        o.k_scale = -1.f;
+        o.v_scale = 1.f;
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(), P(), 64, 1, (const int32_t*)P(), (const int32_t*)P(),
+                                  8, 1, 1, 1000, 0, P(), wr, &o, (float*)P(), nullptr, nullptr) == RBA_ERR_SHAPE);
+        EXPECT(rba_decode_relproj(&p, P(), P(), P(), 8, P(), P(), 64, 1, (const int32_t*)P(), (const int32_t*)P(),
+                                  8, 0, 1, 1000, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr) == RBA_OK);
+    }
     {  // the split stage alone takes no sink or gate, and needs a resolved split count
         rba_call_options o;
         memset(&o, 0, sizeof(o));

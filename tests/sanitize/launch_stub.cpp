@@ -45,6 +45,16 @@ hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t) {
     return hipSuccess;
 }
 
+hipError_t launch_rel_rows(const RelRowsArgs& a, hipStream_t) {
+    expect(a.r && a.proj && a.rel, "bias-row pointers");
+    expect(a.d_r == 32 || a.d_r == 64 || a.d_r == 128, "width of r");
+    expect(a.proj_heads == 1 || a.proj_heads == a.Hq, "projection heads");
+    expect(a.rows >= 1 && a.Hq >= 1 && a.R >= 1, "bias-row sizes");
+    expect(a.rows_per_wg >= 1 && (a.rows + a.rows_per_wg - 1) / a.rows_per_wg <= 65535, "bias-row groups");
+    expect((reinterpret_cast<uintptr_t>(a.rel) & 15u) == 0, "bias-row alignment");
+    return hipSuccess;
+}
+
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t) {
     expect(dv == 64 || dv == 128, "dv");
     expect(a.part_o && a.part_lse && a.out && a.pairs >= 1 && a.splits >= 1 && a.splits <= 1024, "combine");

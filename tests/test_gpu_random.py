@@ -1,8 +1,8 @@
 """Randomised GPU parity: seeded draws over the whole argument space of the
 prefill and decode calls (head counts and grouping, value head size, rel
 extent, window, sequence and context lengths, query tokens per sequence,
-split count, and the optional terms), each checked against the float64
-oracle at the parity bar. The draws are fixed by their seeds, so every run
+split count, the optional terms, and r in place of rel), each checked
+against the float64 oracle at the parity bar. The draws are fixed by their seeds, so every run
 checks the same cases; each is small enough for the oracle to finish in well
 under a second.
 """
@@ -57,6 +57,8 @@ def decode_case(seed):
     lens = [max(n_q, rnd.choice([1, 100, 128, 129, 1000, 2500, 6000])) for _ in range(batch)]
     splits = rnd.choice([0, 0, 1, 2, 7, 40])
     opts = dict(kv_fp8=rnd.random() < 0.3, gated=rnd.random() < 0.25, logpos=rnd.random() < 0.25)
+    if rnd.random() < 0.25:   # bias rows made from r
+        opts.update(d_r=rnd.choice([32, 64, 128]), proj_heads=rnd.choice([1, Hq]))
     return (batch, n_q, lens, Hq, Hkv, dv, R, Wn), splits, opts
 
 

@@ -70,6 +70,10 @@ WORKLOADS["global_chunked_prefill_32k_logpos"] = dict(WORKLOADS["global_chunked_
 WORKLOADS["global_chunked_prefill_32k_fp8"] = dict(WORKLOADS["global_chunked_prefill_32k"], kv_fp8=True)
 WORKLOADS["paged_decode_16x8k_128k_disjoint_logpos"] = dict(WORKLOADS["paged_decode_16x8k_128k_disjoint"],
                                                           logpos=True)
+# Decode workloads whose bias rows are made from r (width 64) and one shared
+# projection instead of being given.
+for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k"):
+    WORKLOADS[_name + "_relproj"] = dict(WORKLOADS[_name], d_r=64)
 # The decode workloads again over e4m3 K/V caches.
 for _name in ("paged_decode_16x8k_128k_disjoint", "verify_decode_b1_100k", "verify_decode_b8_100k"):
     WORKLOADS[_name + "_fp8"] = dict(WORKLOADS[_name], kv_fp8=True)
@@ -236,13 +240,15 @@ def make_prefill(seed: int, q_lens: List[int], ctx_lens: List[int], Hq: int, Hkv
 def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: int, W: int,
                 seq_lens: Optional[List[int]] = None, len_range=None, seq_len: Optional[int] = None,
                 pool_blocks: Optional[int] = None, scale: Optional[float] = None, kv_fp8: bool = False,
-                gated: bool = False, logpos: bool = False) -> Batch:
+                gated: bool = False, logpos: bool = False, d_r: int = 0, proj_heads: int = 1) -> Batch:
     """`batch` sequences decoding n_q tokens each. Lengths: explicit, one fixed
     `seq_len`, or uniform integers in `len_range` (inclusive). With
     pool_blocks=None every sequence gets its own blocks (one global
     permutation of a pool of exactly the needed size); otherwise each sequence
     takes the first blocks of its own permutation of a `pool_blocks` pool, so
-    blocks may be shared between sequences (read-only aliasing)."""
+    blocks may be shared between sequences (read-only aliasing). With d_r > 0
+    the bias comes from r and a projection drawn as in make_prefill (rel is
+    then None)."""
     gen = torch.Generator().manual_seed(seed)
     if seq_lens is None:
         if seq_len is not None:
@@ -257,7 +263,13 @@ def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: 
     q = _bf16((batch * n_q, Hq, HEAD_DIM), gen)
     k_cache = _bf16((num_blocks, Hkv, BLOCK, HEAD_DIM), gen)
     v_cache = _bf16((num_blocks, Hkv, BLOCK, dv), gen)
-    rel = _randn_into(torch.empty((batch * n_q, Hq, R), dtype=torch.float32), gen, 0.5)
+    rel, relproj = None, {}
+    if d_r > 0:
+        relproj["r"] = _bf16((batch * n_q, Hq, d_r), gen)
+        relproj["proj"] = _randn_into(torch.empty((proj_heads, R, d_r), dtype=torch.bfloat16), gen,
+                                      0.5 / d_r ** 0.5)
+    else:
+        rel = _randn_into(torch.empty((batch * n_q, Hq, R), dtype=torch.float32), gen, 0.5)
     tables = []
     if pool_blocks is None:
         order = torch.randperm(num_blocks, generator=gen).tolist()
@@ -281,7 +293,7 @@ def make_decode(seed: int, batch: int, n_q: int, Hq: int, Hkv: int, dv: int, R: 
                  q=q, k_cache=k_cache, v_cache=v_cache, rel=rel,
                  seq_lens=torch.tensor(seq_lens, dtype=torch.int32),
                  block_tables=_tables_tensor(tables, max(nblk)), n_q=n_q,
-                 q_lens=[n_q] * batch, max_q_len=n_q, max_seq_len=max(seq_lens), **kw)
+                 q_lens=[n_q] * batch, max_q_len=n_q, max_seq_len=max(seq_lens), **kw, **relproj)
 
 
 def chunk_of(full: Batch, c: int, chunk: int) -> Batch:
