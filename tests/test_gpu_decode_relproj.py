@@ -131,3 +131,30 @@ def test_decode_relproj_writes_only_out_lse_and_workspace():
         assert bool((torch.cat([fo[:GUARD], fo[GUARD + out.numel():]]) == CANARY).all()), "out guard"
         assert bool((torch.cat([fl[:GUARD], fl[GUARD + lse.numel():]]) == CANARY).all()), "lse guard"
         assert torch.isfinite(out).all()
+
+
+def test_decode_relproj_graph_capture_replay():
+    """The bias-row kernel, the split kernel and the merge captured in one
+    graph: every replay, with eager work between them, reproduces the eager
+    output."""
+    say("decode relproj graph capture")
+    b = W.make_decode(74, 2, 4, 64, 8, 64, 1024, 0, seq_lens=[2500, 6000], d_r=64, proj_heads=1).to(DEV)
+    need = rba.relproj_workspace_size(64, 8, 64, 1024, 0, b.scale, 2, 4, b.max_seq_len)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty((8, 64, 64), device=DEV)
+    eager = run_decode(b, workspace=ws)[0].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_decode(b, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_decode(b, workspace=ws, out=out)
+    for _ in range(3):
+        out.fill_(7.0)
+        ws.fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        run_decode(W.make_decode(1, 1, 1, 32, 8, 128, 1024, 0, seq_lens=[500], d_r=32).to(DEV))
