@@ -795,7 +795,8 @@ int rba_decode_relproj(const rba_attn_params* params, const void* q, const void*
     const size_t need = off + rel_rows_bytes(params, batch, n_q);
     if (workspace_bytes < need)
         return fail(RBA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-    if ((int64_t)params->rel_extent * params->num_heads_q * batch * n_q > ((int64_t)1 << 40))
+    if ((int64_t)params->rel_extent * params->num_heads_q * batch * n_q > ((int64_t)1 << 40) ||
+        params->num_heads_q > 65535)
         return fail(RBA_ERR_UNSUPPORTED, "bias rows too large");
     rba::RelRowsArgs ra;
     ra.r = static_cast<const uint16_t*>(r);
@@ -813,7 +814,7 @@ int rba_decode_relproj(const rba_attn_params* params, const void* q, const void*
         int64_t rpw = 1;
         while (rpw < ra.rows && (xy * ceil_div(ra.rows, rpw) > 3LL * device_cus() || ceil_div(ra.rows, rpw) > 65535))
             rpw *= 2;
-        ra.rows_per_wg = (int32_t)rpw;
+        ra.rows_per_wg = (int32_t)(rpw < ra.rows ? rpw : ra.rows);
     }
     hipError_t e = rba::launch_rel_rows(ra, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "bias rows launch");

@@ -318,3 +318,34 @@ def test_call_options_marshalling():
     declared = re.findall(r"\b(\w+)\s*[;,]", body)
     assert declared == names
     assert rba.call_options(4, 2) is None
+
+
+def test_decode_relproj_checks_before_any_launch():
+    """rba_decode_relproj: the producer's arguments, the decode's and the
+    workspace (partials, then the bias rows from the next multiple of 256
+    bytes) are checked on the host before the first launch."""
+    lib = rba.lib()
+    d = dprm()
+    ws = lib.rba_decode_workspace_size(ctypes.byref(d), 16, 1, 131072, 0)
+    wr = lib.rba_decode_relproj_workspace_size(ctypes.byref(d), 16, 1, 131072, 0)
+    assert wr == (ws + 255) // 256 * 256 + 16 * 1 * 32 * 1024 * 4
+    assert lib.rba_decode_relproj_workspace_size(ctypes.byref(d), 16, 0, 131072, 0) == 0
+
+    def call(r=P, proj=P, d_r=64, ph=1, nbytes=wr, o=None, batch=16):
+        return lib.rba_decode_relproj(ctypes.byref(d), P, P, P, 2560, r, proj, d_r, ph, P, P, 1024, batch, 1,
+                                      131072, 0, P, nbytes, o, P, None, None)
+
+    assert call(d_r=48) == rba.RBA_ERR_UNSUPPORTED
+    assert call(d_r=16) == rba.RBA_ERR_UNSUPPORTED
+    assert call(ph=3) == rba.RBA_ERR_SHAPE
+    assert call(r=None) == rba.RBA_ERR_NULL
+    assert "q/r/seq_lens" in rba.last_error()
+    assert call(proj=None) == rba.RBA_ERR_NULL
+    assert call(r=P + 8) == rba.RBA_ERR_UNSUPPORTED
+    assert call(proj=P + 4) == rba.RBA_ERR_UNSUPPORTED
+    assert call(nbytes=wr - 1) == rba.RBA_ERR_WORKSPACE
+    assert call(nbytes=ws) == rba.RBA_ERR_WORKSPACE          # room for the partials only
+    o = rba.CallOptions()
+    o.kv_e4m3, o.k_scale, o.v_scale = 1, 0.0, 1.0
+    assert call(o=ctypes.byref(o)) == rba.RBA_ERR_SHAPE
+    assert call(batch=0, nbytes=0) == rba.RBA_OK            # empty call, no launch
