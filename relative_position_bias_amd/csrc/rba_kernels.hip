@@ -666,7 +666,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     id /= A.batch;
     const int hc = id % A.n_hc;
     id /= A.n_hc;
-    const int qt = A.n_qt - 1 - id;  // heavy (late) tiles first
+    // Without a window the late tiles (more keys) go first. With one every
+    // tile past the first window has the same work, and ascending order
+    // measured faster for the in-kernel-bias kernel (equal for the other).
+    const int qt = A.W > 0 ? id : A.n_qt - 1 - id;
 
     const int q_start = A.cu_q[b];
     const int q_len = A.cu_q[b + 1] - q_start;
@@ -922,7 +925,10 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     id /= A.batch;
     const int hc = id % A.n_hc;
     id /= A.n_hc;
-    const int qt = A.n_qt - 1 - id;  // heavy (late) tiles first
+    // Without a window the late tiles (more keys) go first. With one every
+    // tile past the first window has the same work, and ascending order
+    // measured faster for the in-kernel-bias kernel (equal for the other).
+    const int qt = A.W > 0 ? id : A.n_qt - 1 - id;
 
     const int q_start = A.cu_q[b];
     const int q_len = A.cu_q[b + 1] - q_start;
