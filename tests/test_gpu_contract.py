@@ -169,3 +169,33 @@ def test_decode_writes_only_out_lse_and_workspace(case):
         assert untouched(fw, need), f"workspace guard, splits={splits}"
         assert untouched(fo, out.numel()) and untouched(fl, lse.numel()), f"out/lse guard, splits={splits}"
         assert torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------------------------
+# calls on several streams at once: each with its own outputs and workspace,
+# every result equals the same call made alone
+# ---------------------------------------------------------------------------
+def test_concurrent_calls_on_separate_streams():
+    say("concurrent calls on four streams")
+    decs = [W.make_decode(80 + i, 3, n_q, 32, 8, 128, 1024, 0, seq_lens=[4000, 900, 7000]).to(DEV)
+            for i, n_q in enumerate((1, 4))]
+    pres = [W.make_prefill(90 + i, [300, 64], [800, 0], 8, 2, 128, 512, w).to(DEV) for i, w in enumerate((0, 200))]
+    alone = [run_decode(b)[0].clone() for b in decs] + [run_prefill(b)[0].clone() for b in pres]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    outs = [torch.full_like(a, 7.0) for a in alone]
+    wss = [torch.empty(rba.workspace_size(32, 8, 128, 1024, 0, b.scale, 3, b.n_q, b.max_seq_len), dtype=torch.uint8,
+                       device=DEV) for b in decs]
+    cur = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(cur)
+    for rep in range(5):
+        for i, b in enumerate(decs):
+            run_decode(b, workspace=wss[i], out=outs[i], stream=streams[i])
+        for i, b in enumerate(pres):
+            run_prefill(b, out=outs[2 + i], stream=streams[2 + i])
+    for s in streams:
+        cur.wait_stream(s)
+    torch.cuda.synchronize()
+    for i, (o, a) in enumerate(zip(outs, alone)):
+        assert torch.equal(o, a), f"call {i}"
