@@ -55,7 +55,12 @@
 //     prefill copies a block's (or stage's) bytes into a staging area of LDS
 //     and widens them there, between two barriers, into the bf16 layouts its
 //     compute loop reads. K's scale folds into the score scale, V's into the
-//     output.
+//     output. Over e4m3 K the decode takes the head dimension in another
+//     order, the same for q and K, so that each 16-byte load of a K row feeds
+//     two score MFMAs.
+//   * Decode with the bias made from r: a step's bias is only batch * n_q
+//     rows, so a small separate kernel writes them into the workspace and the
+//     decode kernels read them like a materialised rel.
 //   * Decode: each of the 4 waves of a workgroup streams its own 32-key
 //     subtile of every block of the split without any barrier: K goes straight
 //     from HBM into MFMA operand registers, V into a wave-private LDS tile.
