@@ -72,14 +72,14 @@ def check(b_cpu, what, **kw):
     assert lmx <= 1e-3, f"{what}: lse max err {lmx:.3e}"
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_random_prefill(seed):
     case, opts = prefill_case(seed)
     say(f"random prefill {seed}: {case} {opts}")
     check(W.make_prefill(3000 + seed, *case, **opts), f"prefill seed {seed} {case} {opts}")
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_random_decode(seed):
     (batch, n_q, lens, Hq, Hkv, dv, R, Wn), splits, opts = decode_case(seed)
     say(f"random decode {seed}: B{batch} n_q{n_q} {lens} H{Hq}/{Hkv} dv{dv} R{R} W{Wn} splits{splits} {opts}")
