@@ -1,10 +1,10 @@
 """Randomised GPU parity: seeded draws over the whole argument space of the
 prefill and decode calls (head counts and grouping, value head size, rel
 extent, window, sequence and context lengths, query tokens per sequence,
-split count, the optional terms, r in place of rel, and aliased pools),
-each checked against the float64 oracle at the parity bar. The draws are
-fixed by their seeds, so every run checks the same cases; each is small
-enough for the oracle to finish in well under a second.
+split count, score scale, the optional terms, r in place of rel, and
+aliased pools), each checked against the float64 oracle at the parity bar.
+The draws are fixed by their seeds, so every run checks the same cases;
+each is small enough for the oracle to finish in well under a second.
 """
 import random
 import sys
@@ -42,6 +42,8 @@ def prefill_case(seed):
         opts.update(d_r=rnd.choice([32, 64, 128]), proj_heads=rnd.choice([1, Hq]))
     if rnd.random() < 0.25:   # e4m3 caches
         opts.update(kv_fp8=True)
+    if rnd.random() < 0.25:   # a score scale other than 1/sqrt(128)
+        opts.update(scale=rnd.choice([0.03, 0.25]))
     return (q_lens, ctx, Hq, Hkv, dv, R, Wn), opts
 
 
@@ -61,6 +63,8 @@ def decode_case(seed):
         opts.update(d_r=rnd.choice([32, 64, 128]), proj_heads=rnd.choice([1, Hq]))
     if rnd.random() < 0.2:    # sequences drawing their blocks from one small shared pool (aliased blocks)
         opts.update(pool_blocks=max((L + 127) // 128 for L in lens) + rnd.randint(0, 8))
+    if rnd.random() < 0.25:   # a score scale other than 1/sqrt(128)
+        opts.update(scale=rnd.choice([0.03, 0.25]))
     return (batch, n_q, lens, Hq, Hkv, dv, R, Wn), splits, opts
 
 
