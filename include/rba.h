@@ -254,12 +254,14 @@ int rba_validate_decode(const rba_attn_params* params,
  * Split plan (host only, pure function). Returns the number of KV splits
  * rba_decode uses for num_splits = 0 on a device with `num_cus` compute units.
  * Work units are (sequence, KV head, 32-column group, split); up to two run
- * per CU at a time. If one unit per CU (num_cus units) covers max_seq_len
- * with at most 32 blocks per split, and the kernel that runs keeps the next
- * block's loads in flight (G * n_q <= 16, or head_dim_v <= 64), that is used;
- * else if one round of two per CU (2 * num_cus units) covers it with at most
- * 128 blocks per split, that round; otherwise splits of ~32 blocks of
- * max_seq_len. Never fewer than ~16 blocks per split, at most 256 splits.
+ * per CU at a time. With 33 to 64 columns (G * n_q) one unit covers both
+ * column groups and one runs per CU. If one unit per CU (num_cus units)
+ * covers max_seq_len with at most 32 blocks per split, and the kernel that
+ * runs keeps the next block's loads in flight (G * n_q <= 16, head_dim_v <=
+ * 64, or 33 to 64 columns), that is used; else if one round of units (two per
+ * CU, one with 33 to 64 columns) covers it with at most 128 blocks per split,
+ * that round; otherwise splits of ~32 blocks of max_seq_len. Never fewer than
+ * ~16 blocks per split, at most 256 splits.
  * Returns a negative RBA_ERR_* code on bad arguments.
  */
 int32_t rba_decode_plan_splits(const rba_attn_params* params, int32_t batch, int32_t n_q,

@@ -123,11 +123,15 @@ int32_t plan_splits(const rba_attn_params* p, int32_t batch, int32_t n_q, int32_
     // and short sequences spread over many workgroups. Always at least ~16
     // blocks per split and at most 256 splits.
     const int64_t G = p->num_heads_q / p->num_heads_kv;
-    const int64_t n_cg = ceil_div(G * n_q, 32);
+    // 33 to 64 columns: one 8-wave workgroup covers both column groups
+    // (over bf16 K/V; over e4m3 K/V the two groups run as two workgroups on
+    // the same plan), one per CU, double-buffering its blocks
+    const bool paired = G * n_q > 32 && G * n_q <= 64;
+    const int64_t n_cg = paired ? 1 : ceil_div(G * n_q, 32);
     const int64_t nb_eff = decode_nb_eff(p, n_q, max_seq_len);
     const int64_t units = (int64_t)batch * p->num_heads_kv * n_cg;
-    const bool prefetching = G * n_q <= 16 || p->head_dim_v <= 64;
-    const int64_t fill1 = (int64_t)num_cus / units, fill2 = (2LL * num_cus) / units;
+    const bool prefetching = G * n_q <= 16 || p->head_dim_v <= 64 || paired;
+    const int64_t fill1 = (int64_t)num_cus / units, fill2 = ((paired ? 1LL : 2LL) * num_cus) / units;
     int64_t want;
     if (prefetching && fill1 >= 1 && ceil_div(nb_eff, fill1) <= 32)
         want = fill1;
@@ -263,7 +267,7 @@ rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void*
                             const void* v_cache, int32_t num_blocks, const float* rel,
                             const int32_t* seq_lens, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, int32_t batch, int32_t n_q, int32_t max_seq_len,
-                            int32_t splits, void* workspace) {
+                            int32_t splits, void* workspace, bool kv8) {
     rba::DecodeArgs a;
     const int G = p->num_heads_q / p->num_heads_kv;
     const size_t pairs = (size_t)batch * n_q * p->num_heads_q;
@@ -288,7 +292,8 @@ rba::DecodeArgs decode_args(const rba_attn_params* p, const void* q, const void*
     a.kv8 = 0;
     a.lscale = nullptr;
     a.n_q = n_q;
-    a.n_cg = (int32_t)ceil_div((int64_t)G * n_q, 32);
+    // 33 to 64 columns over bf16 K/V: one workgroup for both column groups
+    a.n_cg = (!kv8 && G * n_q > 32 && G * n_q <= 64) ? 1 : (int32_t)ceil_div((int64_t)G * n_q, 32);
     a.splits = splits;
     a.bps = (int32_t)ceil_div(decode_nb_eff(p, n_q, max_seq_len), splits);
     a.wide = (int64_t)batch * a.Hkv * a.n_cg * splits <= device_cus() ? 1 : 0;
@@ -476,7 +481,7 @@ int decode_impl(const rba_attn_params* params, const void* q, const void* k_cach
     if (rc || nothing) return rc;
     if (need_lscale && o.lscale == nullptr) return fail(RBA_ERR_NULL, "logit_scale is NULL");
     rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace);
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, workspace, o.kv8);
     if (o.kv8) {
         a.c1 = (float)((double)params->scale * (double)o.k_scale * 1.4426950408889634);
         a.v_scale = o.v_scale;
@@ -724,7 +729,7 @@ int rba_decode_noalloc(const rba_attn_params* params, const void* q, const void*
     hipError_t e = rba::noalloc_scratch(&scratch);
     if (e != hipSuccess) return hip_fail(e, "scratch address");
     rba::DecodeArgs a = decode_args(params, q, k_cache, v_cache, num_blocks, rel, seq_lens, block_tables,
-                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, scratch);
+                                    max_blocks_per_seq, batch, n_q, max_seq_len, splits, scratch, false);
     hipStream_t s = static_cast<hipStream_t>(stream);
     e = rba::launch_decode_split(a, params->head_dim_v, s);
     if (e != hipSuccess) return hip_fail(e, "decode split launch");

@@ -66,7 +66,9 @@
 //     from HBM into MFMA operand registers, V into a wave-private LDS tile.
 //     Each block is read once for all G * n_q columns; splits of the block
 //     range go to different workgroups and a small kernel merges them by
-//     log-sum-exp.
+//     log-sum-exp. With 33 to 64 columns over bf16 K/V one 8-wave workgroup
+//     takes both 32-column groups and copies each block into LDS once for
+//     them (prefill-style, double-buffered).
 //   * Work-unit order puts the KV head in the fastest position of blockIdx so
 //     that, with workgroups dealt round-robin to the 8 XCDs, all workgroups of
 //     one KV head (which share its K/V) land on the same XCD and its L2.
@@ -1581,6 +1583,217 @@ __global__ void __launch_bounds__(512) decode_split8_logpos_kernel(const DecodeA
 }
 
 // ---------------------------------------------------------------------------
+// Decode for 33 to 64 columns (G * n_q), bf16 K/V: one workgroup of 8 waves
+// per (sequence, KV head, split) covers both 32-column groups. Waves 0-3
+// take group 0 and waves 4-7 group 1, wave w subtile w & 3 of every block, so
+// the two waves of a subtile share its K/V: each 128-key block is copied from
+// HBM into LDS once (global_load_lds into double buffers, in the prefill's
+// swizzled-K / rotated-V layouts, all 8 waves issuing the copies) and both
+// groups read it there, instead of each group's workgroup loading every
+// block into its own registers. The next block's copy overlaps the current
+// block's compute; the bias of the next block's subtile is requested during
+// the current one. Scores, softmax and P.V are the prefill's. The partial
+// state of each group is merged over its 4 waves through LDS, as in the other
+// decode kernels.
+// ---------------------------------------------------------------------------
+template <int DV>
+struct PairLds {
+    static constexpr int KV_BYTES = 2 * BS * DQK * 2 + 2 * BS * DV * 2;   // K0, K1, V0, V1
+    static constexpr int MERGE = 8 * 32 * DV * 4 + 2 * 8 * 32 * 4;
+    static constexpr int TOTAL = KV_BYTES > MERGE ? KV_BYTES : MERGE;
+};
+
+template <int DV, bool LS>
+__device__ __forceinline__ void decode_pair_body(const DecodeArgs A) {
+    __shared__ __attribute__((aligned(16))) char smem[PairLds<DV>::TOTAL];
+    __bf16* const K0 = reinterpret_cast<__bf16*>(smem);
+    __bf16* const K1 = K0 + BS * DQK;
+    __bf16* const V0 = K1 + BS * DQK;
+    __bf16* const V1 = V0 + BS * DV;
+
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31,
+              hh = lane >> 5;
+    const int grp = wid >> 2, sub = wid & 3;
+    int id = blockIdx.x;
+    const int g = id % A.Hkv;
+    id /= A.Hkv;
+    const int b = id % A.batch;
+    const int split = id / A.batch;
+
+    const int L = A.seq_lens[b];
+    const int ncols = A.G * A.n_q;   // 33 .. 64
+    const int c = grp * 32 + n;
+    const bool real = c < ncols;
+    const int tt = real ? c / A.G : 0;
+    const int hl = real ? c % A.G : 0;
+    const int h = g * A.G + hl;
+    const long long trow = (long long)(b * A.n_q + tt) * A.Hq + h;
+    const float fls = (LS && real) ? A.lscale[b * A.n_q + tt] : 1.f;  // the row's logit scale
+    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
+
+    Cols<DV> C;
+    C.pos = real ? L - A.n_q + tt : -1;
+    C.relrow = A.rel + trow * A.R;
+    const int c_hi = min(grp * 32 + 31, ncols - 1);
+    C.w_lo = L - A.n_q + (grp * 32) / A.G;
+    C.w_hi = L - A.n_q + c_hi / A.G;
+    C.phantom = c_hi < grp * 32 + 31;
+    load_q(C, A.q + trow * DQK, lane);
+    init_acc(C);
+
+    const int nb = L / BS + (L % BS != 0);
+    const int kb_first = A.W > 0 ? max(0, (L - A.n_q) - A.W + 1) / BS : 0;
+    const int s_lo = kb_first + split * A.bps;
+    // a device length outside the caller's contract gives NaN rows (as the
+    // other decode kernels); no table entry past the row is read
+    const bool len_bad = L < A.n_q || nb > A.max_blocks || nb > kb_first + A.splits * A.bps;
+    const int s_hi = len_bad ? s_lo : min(s_lo + A.bps, nb);
+    const int ka = s_lo, kz = s_hi - 1;
+    bool bad = len_bad;
+
+    const int* const tab = A.tables + (long long)b * A.max_blocks;
+    int tab_base = ka;
+    int tabv = (ka + lane <= kz) ? tab[ka + lane] : -1;
+    auto block_base = [&](int kb, bool& okk) -> size_t {
+        if (kb - tab_base >= 64) {
+            tab_base += 64;
+            tabv = (tab_base + lane <= kz) ? tab[tab_base + lane] : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
+        okk = phys >= 0 && phys < A.num_blocks;
+        return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
+    };
+    auto rel_active = [&](int js) { return !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
+    auto rel_inside = [&](int js) { return !C.phantom && C.w_lo - js - 31 >= 0 && C.w_hi - js < A.R; };
+
+    int koff[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) koff[st] = n * DQK + 8 * ((2 * st + hh) ^ (n & 15));
+    int vbo[DV / 32];
+    {
+        const int gq = lane >> 4, j = lane & 15, vr = 8 * (gq >> 1) + (j >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+            vbo[dt] = vr * DV + 32 * ((dt + vrot<DV>(vr)) & (DV / 32 - 1)) + 16 * (gq & 1) + 4 * (j & 3);
+    }
+
+    bool ok = false;
+    RelVals rv[2];  // bias of this block's subtile and of the next block's
+    if (ka <= kz) {
+        const size_t base = block_base(ka, ok);
+        if (ok) kv_dma<DV, 8>(K0, V0, A.k + base * DQK, A.v + base * DV, L - ka * BS, wid, lane);
+        if (rel_active(ka * BS + 32 * sub))
+            rel_fetch(rv[0], C.relrow, C.pos, ka * BS + 32 * sub, A.R, rel_inside(ka * BS + 32 * sub), lane);
+    }
+
+    auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn, int kb, const RelVals& rcur,
+                    RelVals& rnext) {
+        vm_wait_all();
+        lds_barrier();  // this block's copy is in; every wave is done with the other buffers
+        const bool ok_cur = ok;
+        bad = bad || !ok_cur;
+        if (kb < kz) {
+            const size_t base = block_base(kb + 1, ok);
+            if (ok) kv_dma<DV, 8>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - (kb + 1) * BS, wid, lane);
+        }
+        const int js = kb * BS + 32 * sub;
+        const bool computed = ok_cur && !masked_all(C, js, A.W);
+        float x[16];
+        float M = -INFINITY;
+        if (computed) {
+            const f32x16 sc = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
+            M = sm_scores_rv(C, sc, rel_active(js), rcur, rel_inside(js), need_mask_of(C, js, A.W), js, A.W, A.R,
+                             c1f, l2f, lane, x);
+        }
+        const int jn = js + BS;  // this wave's subtile of the next block
+        if (kb < kz && rel_active(jn)) rel_fetch(rnext, C.relrow, C.pos, jn, A.R, rel_inside(jn), lane);
+        if (computed) {
+            if (__any(!C.m_set || sm_trigger(C, M))) {
+                if (__any(!C.m_set)) sm_init_ref(C, M, x);
+                if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+            }
+            bf16x8 pb[2];
+            sm_probs(C, x, pb);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                for (int dt = 0; dt < DV / 32; ++dt)
+                    C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * cc) * DV, vbo[dt], DV), pb[cc], C.O[dt]);
+            }
+        }
+    };
+    for (int kb = ka; kb <= kz;) {
+        step(K0, V0, K1, V1, kb, rv[0], rv[1]);
+        if (kb == kz) break;
+        ++kb;
+        step(K1, V1, K0, V0, kb, rv[1], rv[0]);
+        if (kb == kz) break;
+        ++kb;
+    }
+
+    // Merge each group's 4 partial states through LDS (the K/V buffers are
+    // free once every wave has passed the barrier).
+    __syncthreads();
+    float* Om = reinterpret_cast<float*>(smem);   // [8][32][DV]
+    float* Mm = Om + 8 * 32 * DV;                 // [8][32] reference max (or -inf)
+    float* Lm = Mm + 8 * 32;                      // [8][32] row sums
+    const float l_tot = C.l_sum + xor32(C.l_sum);
+    const bool any_bad = __syncthreads_or(bad);
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = C.O[dt][4 * q4 + k];
+            *reinterpret_cast<f32x4*>(Om + (wid * 32 + n) * DV + 32 * dt + 8 * q4 + 4 * hh) = o;
+        }
+    }
+    // a column that saw any key has l_tot >= 1 (its reference's own term);
+    // one that saw none has l_tot = 0 (its reference was never set)
+    if (hh == 0) {
+        Mm[wid * 32 + n] = l_tot > 0.f ? C.m_ref : -INFINITY;
+        Lm[wid * 32 + n] = l_tot;
+    }
+    __syncthreads();
+
+    for (int e = tid; e < 64 * DV; e += 512) {
+        const int col = e / DV, dv = e % DV;  // column 0 .. 63 = group * 32 + lane column
+        if (col >= ncols) continue;
+        const int w0 = 4 * (col >> 5), cn = col & 31;
+        float mw[4], Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = Mm[(w0 + w) * 32 + cn];
+            Mx = fmaxf(Mx, mw[w]);
+        }
+        float den = 0.f, num = 0.f;
+        if (Mx > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = __builtin_amdgcn_exp2f(mw[w] - Mx);  // exp2(-inf) = 0
+                den += f * Lm[(w0 + w) * 32 + cn];
+                num += f * Om[((w0 + w) * 32 + cn) * DV + dv];
+            }
+        }
+        const int ctt = col / A.G, chl = col % A.G;
+        const long long prow = ((long long)(b * A.n_q + ctt) * A.Hq + (g * A.G + chl)) * A.splits + split;
+        A.part_o[prow * DV + dv] = any_bad ? NAN : (Mx > -INFINITY ? num / den : 0.f);
+        if (dv == 0) A.part_lse[prow] = any_bad ? NAN : (Mx > -INFINITY ? (Mx + __log2f(den)) * LN2 : -INFINITY);
+    }
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) decode_pair_kernel(const DecodeArgs A) {
+    decode_pair_body<DV, false>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) decode_pair_logpos_kernel(const DecodeArgs A) {
+    decode_pair_body<DV, true>(A);
+}
+
+// ---------------------------------------------------------------------------
 // Split-KV decode, 16-column variant (G * n_q <= 16, e.g. one token of 4
 // query heads per KV head). Same work split as decode_split_kernel, but the
 // scores use v_mfma_f32_16x16x32_bf16 with 16 (head, token) columns per wave,
@@ -2135,6 +2348,13 @@ void launch_split_t(const DecodeArgs& a, dim3 g, hipStream_t s) {
         if (LS) hipLaunchKernelGGL((decode16_split_logpos_kernel<DV, KV8>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((decode16_split_kernel<DV, KV8>), g, blk, 0, s, a);
         return;
+    }
+    if constexpr (!KV8) {
+        if (a.n_cg == 1 && a.G * a.n_q > 32) {  // both column groups in one workgroup
+            if (LS) hipLaunchKernelGGL((decode_pair_logpos_kernel<DV>), g, dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((decode_pair_kernel<DV>), g, dim3(512), 0, s, a);
+            return;
+        }
     }
     if constexpr (DV == 64 && KV8) {
         if (a.wide) {

@@ -36,7 +36,10 @@ hipError_t launch_prefill_relproj(const PrefillArgs& a, int dv, hipStream_t s) {
 hipError_t launch_decode_split(const DecodeArgs& a, int dv, hipStream_t) {
     expect(dv == 64 || dv == 128, "dv");
     expect(a.q && a.k && a.v && a.rel && a.seq_lens && a.tables && a.part_o && a.part_lse, "pointers");
-    expect(a.Hq == a.Hkv * a.G && a.n_cg * 32 >= a.G * a.n_q && a.n_q >= 1, "columns");
+    // 33 to 64 columns over bf16 K/V run as one workgroup for both groups
+    expect(a.Hq == a.Hkv * a.G && a.n_q >= 1 &&
+               (a.n_cg * 32 >= a.G * a.n_q || (a.n_cg == 1 && a.kv8 == 0 && a.G * a.n_q <= 64)),
+           "columns");
     expect(a.splits >= 1 && a.bps >= 1 && a.batch >= 1, "split plan");
     // the splits cover the longest visible range
     const long long nb_max = (a.max_blocks > 0) ? a.max_blocks : 0;
