@@ -432,7 +432,7 @@ def main():
         t = sum(ms[k] for k in ks) / 1e3
         f = sum(calls[k][3] for k in ks)
         nb = sum(calls[k][4] for k in ks)
-        kname = f"prefill_kernel<{b.dv}, {'true' if b.W > 0 else 'false'}>"
+        kname = f"prefill_ring_kernel<{b.dv}>" if b.W > 0 else f"prefill_kernel<{b.dv}>"
         if f / PEAK_MFMA_BF16 >= nb / PEAK_HBM:
             achieved = f / t / 1e12
             blk = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),

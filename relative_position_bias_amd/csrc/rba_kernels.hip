@@ -26,8 +26,10 @@
 //     transposed writes.
 //   * The bias is "sheared": element (column n, key j) needs rel[t_n, h_n,
 //     i_n - j], and a lane's 8 consecutive keys are 8 consecutive (falling)
-//     distances of its own rel row. The prefill loads them straight into
-//     registers (two 16-byte loads per run); the decode loads, with 16-byte
+//     distances of its own rel row. The prefill without a window loads them
+//     straight into registers (two 16-byte loads per run); the windowed
+//     prefill stages them through a per-column LDS ring (below); the decode
+//     loads, with 16-byte
 //     loads, the aligned superset of its 32 rel row segments (32 rows x 36
 //     floats), parks it in an LDS band and reads every lane's 16 values back
 //     along the shear. Subtiles whose distances are all >= R skip rel
@@ -43,13 +45,15 @@
 //     (one barrier per block); the next subtile's bias comes straight into
 //     registers. The block-table slice sits in a register (one entry per
 //     lane) so no load waits on a table read.
+//   * Windowed prefill, where every subtile carries bias: each wave keeps the
+//     last two 32-distance bands of its columns' rel rows in a per-column
+//     LDS ring, loaded 128 bytes of a row per 8 lanes, and reads each lane's
+//     values back along the shear. The ring leaves room for half-block K/V
+//     stages only.
 //   * Prefill with the bias made in the kernel (rel = r @ rel_logits_proj,
 //     "Attention with a relative bias"): each wave forms the 63-distance band
 //     of a subtile from r (an MFMA operand held for the whole sweep) and the
-//     projection rows (from L2) with d_r / 16 more MFMAs, keeps the last two
-//     32-distance bands in a per-column LDS ring, and reads each lane's
-//     values back along the shear. The ring leaves room for half-block K/V
-//     stages only.
+//     projection rows (from L2) with d_r / 16 more MFMAs into the same ring.
 //   * e4m3 (FP8) K/V caches ("vLLM TML Inkling Support", "Future Roadmap"):
 //     the decode widens each piece to bf16 in registers as it is loaded; the
 //     prefill copies a block's (or stage's) bytes into a staging area of LDS
@@ -652,9 +656,11 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
 // single pair of bf16 buffers K0 / V0 between two barriers; the compute loop
 // is the bf16 one. The K scale is folded into c1, the V scale into the
 // output.
-template <int DV, bool WIN, bool LS, bool KV8 = false>
+// Windowed calls go to prefill_ring_body; the tile logic here still covers
+// any window.
+template <int DV, bool LS, bool KV8 = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
-    constexpr int NW = WIN ? 8 : 4;  // waves that issue the K/V copies
+    constexpr int NW = 4;  // waves that issue the K/V copies
     __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 ? 8 : BS * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 V0[BS * DV];
@@ -673,10 +679,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     id /= A.batch;
     const int hc = id % A.n_hc;
     id /= A.n_hc;
-    // Without a window the late tiles (more keys) go first. With one every
-    // tile past the first window has the same work, and ascending order
-    // measured faster for the in-kernel-bias kernel (equal for the other).
-    const int qt = A.W > 0 ? id : A.n_qt - 1 - id;
+    // The late tiles (more keys) go first.
+    const int qt = A.n_qt - 1 - id;
 
     const int q_start = A.cu_q[b];
     const int q_len = A.cu_q[b + 1] - q_start;
@@ -716,22 +720,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
     const int kb_hi = i_hi / BS;
-    // Block order. A windowed tile spans a few blocks, most of them shared
-    // with its neighbours. Each such tile walks its blocks as a rotation that
-    // starts at its first block whose index is a multiple of RM, the block
-    // count of a tile aligned to the blocks: the tiles with RM blocks then
-    // all read block b at their step b mod RM, at the same time, so a block
-    // that L2 holds for one of them is still there for the others (between
-    // steps the bias streaming through L2 would evict it). Without a window,
-    // or for a span of 64 blocks or more, the order is ascending.
-    int kb_first = kb_lo;
-    if (WIN && kb_hi - kb_lo < 64) {
-        const int RM = (A.W + A.QT - 1 + BS - 1) / BS;
-        const int b0 = kb_lo + (RM - kb_lo % RM) % RM;
-        if (b0 <= kb_hi) kb_first = b0;
-    }
-    const int kb_last = kb_first > kb_lo ? kb_first - 1 : kb_hi;
-    auto next_kb = [&](int kb) { return kb == kb_hi ? kb_lo : kb + 1; };
     const int* tab = A.tables + (long long)b * A.max_blocks;
     bool bad = false;
 
@@ -766,16 +754,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
 
     bool ok = false;
     {
-        const size_t base = block_base(kb_first, ok);
+        const size_t base = block_base(kb_lo, ok);
         if constexpr (KV8) {
             if (ok) kv8_dma<DV, NW>(S8, k8 + base * DQK, v8 + base * DV, wid, lane);
         } else {
-            if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_first * BS, wid, lane);
+            if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, wid, lane);
         }
     }
     RelVals rv[2];  // bias of the current and of the next subtile
-    if (rel_active(kb_first * BS))
-        rel_fetch(rv[0], C.relrow, C.pos, kb_first * BS, A.R, rel_inside(kb_first * BS), lane);
+    if (rel_active(kb_lo * BS)) rel_fetch(rv[0], C.relrow, C.pos, kb_lo * BS, A.R, rel_inside(kb_lo * BS), lane);
 
     // One block: wait for its copy, start the next block's copy into the
     // other buffers (every wave left them at this barrier), compute.
@@ -784,7 +771,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
         lds_barrier();
         const bool ok_cur = ok;
         bad = bad || !ok_cur;
-        const int kbn = kb != kb_last ? next_kb(kb) : -1;  // the next block, if any
+        const int kbn = kb != kb_hi ? kb + 1 : -1;  // the next block, if any
         if constexpr (KV8) {
             kv8_widen<DV>(K0, V0, S8, L - kb * BS, tid);  // this block, bytes -> bf16
             lds_barrier();                                 // widened block visible, S8 free
@@ -801,21 +788,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
         for (int sub = 0; sub < 4; ++sub) {
             const int js = kb * BS + 32 * sub;
             // The next subtile's bias is requested before this subtile's
-            // scores, or (with a window, where every subtile has bias) after
-            // them: the wait for this subtile's bias drains every load issued
-            // before it, so a request placed ahead of it would be waited for
-            // too.
-            auto prefetch_rel = [&]() {
-                const int jn = sub < 3 ? js + 32 : (kbn >= 0 ? kbn * BS : -1);  // the next subtile
-                if (jn >= 0 && rel_active(jn))
-                    rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, jn, A.R, rel_inside(jn), lane);
-            };
-            auto scores = [&](float(&x)[16]) {
-                const f32x16 s = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
-                return sm_scores_rv(C, s, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W), js,
-                                    A.W, A.R, c1f, l2f, lane, x);
-            };
-            auto finish = [&](float M, float(&x)[16]) {
+            // scores.
+            const int jn = sub < 3 ? js + 32 : (kbn >= 0 ? kbn * BS : -1);  // the next subtile
+            if (jn >= 0 && rel_active(jn))
+                rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, jn, A.R, rel_inside(jn), lane);
+            if (ok_cur && !masked_all(C, js, A.W)) {
+                const f32x16 sc = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
+                float x[16];
+                float M = sm_scores_rv(C, sc, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W),
+                                       js, A.W, A.R, c1f, l2f, lane, x);
                 if (__any(!C.m_set || sm_trigger(C, M))) {
                     if (__any(!C.m_set)) sm_init_ref(C, M, x);
                     if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
@@ -828,31 +809,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
                     for (int dt = 0; dt < DV / 32; ++dt)
                         C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * c) * DV, vbo[dt], DV), pb[c], C.O[dt]);
                 }
-            };
-            const bool computed = ok_cur && !masked_all(C, js, A.W);
-            if constexpr (WIN) {
-                float x[16];
-                float M = -INFINITY;
-                if (computed) M = scores(x);
-                prefetch_rel();
-                if (computed) finish(M, x);
-            } else {
-                prefetch_rel();
-                if (computed) {
-                    float x[16];
-                    const float M = scores(x);
-                    finish(M, x);
-                }
             }
         }
     };
-    for (int kb = kb_first;;) {
+    for (int kb = kb_lo;;) {
         step(K0, V0, KB, VB, kb);
-        if (kb == kb_last) break;
-        kb = next_kb(kb);
+        if (++kb > kb_hi) break;
         step(KB, VB, K0, V0, kb);
-        if (kb == kb_last) break;
-        kb = next_kb(kb);
+        if (++kb > kb_hi) break;
     }
 
     if (!wave_active || !real) return;
@@ -860,24 +824,24 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
               A.gate ? A.gate[trow] : INFINITY, lane, KV8 ? A.v_scale : 1.f);
 }
 
-template <int DV, bool WIN>
+template <int DV>
 __global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
-    prefill_body<DV, WIN, false>(A);
+    prefill_body<DV, false>(A);
 }
 
-template <int DV, bool WIN>
+template <int DV>
 __global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A) {
-    prefill_body<DV, WIN, true>(A);
+    prefill_body<DV, true>(A);
 }
 
-template <int DV, bool WIN>
+template <int DV>
 __global__ void __launch_bounds__(512) prefill_fp8_kernel(const PrefillArgs A) {
-    prefill_body<DV, WIN, false, true>(A);
+    prefill_body<DV, false, true>(A);
 }
 
-template <int DV, bool WIN>
+template <int DV>
 __global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillArgs A) {
-    prefill_body<DV, WIN, true, true>(A);
+    prefill_body<DV, true, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,13 +866,34 @@ __global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillAr
 // The ring (32 x 76 floats per wave, 76 KiB for 8 waves) does not fit beside
 // double-buffered whole K/V blocks, so K/V move in half blocks of 64 keys
 // (two subtiles per barrier).
+//
+// The windowed prefill over a materialised rel uses the same ring (DR = 0):
+// band T(jb) is then the rel entries of the 32 distances (w_lo - jb) - 32 ..
+// (w_lo - jb) - 1 of each column's row, which start at the same distance in
+// every row. Eight lanes load one row's 128 bytes, so one load instruction
+// covers 8 rows; loading each lane's own 8-distance runs straight from HBM
+// (as prefill_body does) spreads every instruction over 32 rows, and on the
+// windowed prefill, where every subtile streams bias, the vector memory path
+// then saturates on the number of rows in flight.
 // ---------------------------------------------------------------------------
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
-// DR: the width of r (32, 64 or 128). KV8: e4m3 K/V caches, staged and
-// widened per stage as in prefill_body (one pair of bf16 stage buffers).
+// What a band is made from: projection rows (the A operand of the band MFMAs)
+// or, for DR = 0, four 4-distance pieces of rel rows.
+template <int DR>
+struct BandSrc {
+    bf16x8 p[DR / 16];
+};
+template <>
+struct BandSrc<0> {
+    f32x4 p[4];
+};
+
+// DR: the width of r (32, 64 or 128), or 0 for a materialised rel. KV8: e4m3
+// K/V caches, staged and widened per stage as in prefill_body (one pair of
+// bf16 stage buffers).
 template <int DV, bool LS, int DR, bool KV8 = false>
-__device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
+__device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     constexpr int NW = 8;   // every wave issues copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
@@ -961,8 +946,13 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     C.w_lo = ctx + qa;
     C.w_hi = ctx + qb;
     C.phantom = qb < qa + 31;
-    const uint16_t* proj = A.proj + (size_t)(A.proj_heads == A.Hq ? h : 0) * A.R * DR;
+    const uint16_t* proj = DR > 0 ? A.proj + (size_t)(A.proj_heads == A.Hq ? h : 0) * A.R * DR : nullptr;
     float* ring = ring_all + wid * 32 * RSTRIDE + n * RSTRIDE;  // this lane's column
+    // DR = 0: rel row of column lane >> 3 (the loads of band pieces add 8 k rows)
+    const long long rel_rs = (long long)A.Hq * A.R;
+    const float* relc = DR == 0 && wave_active
+                            ? A.rel + ((long long)(q_start + qa) * A.Hq + h) * A.R + (lane >> 3) * rel_rs
+                            : nullptr;
 
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int s_lo = (A.W > 0 ? max(0, i_lo - A.W + 1) : 0) / HB;
@@ -973,19 +963,44 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
 
     auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
 
-    // Projection rows of band T(jb) as the A operand: lane row a holds the
-    // weights of distance (w_lo - jb) - 32 + a (zero outside [0, R)).
-    auto load_p = [&](bf16x8 (&pv)[DR / 16], int jb) {
-        const int d = C.w_lo - jb - 32 + n;
-        const bool in = (unsigned)d < (unsigned)A.R;
-        const uint16_t* src = proj + (size_t)(in ? d : 0) * DR + 8 * hh;
+    // Sources of band T(jb). DR > 0: projection rows as the A operand, lane
+    // row a holding the weights of distance (w_lo - jb) - 32 + a. DR = 0:
+    // piece k of lane l is column 8 k + (l >> 3), distances (w_lo - jb) - 32
+    // + 4 (l & 7) + 0..3. Zero outside [0, R) and for phantom columns.
+    auto load_p = [&](BandSrc<DR>& pv, int jb) {
+        if constexpr (DR > 0) {
+            const int d = C.w_lo - jb - 32 + n;
+            const bool in = (unsigned)d < (unsigned)A.R;
+            const uint16_t* src = proj + (size_t)(in ? d : 0) * DR + 8 * hh;
 #pragma unroll
-        for (int st = 0; st < DR / 16; ++st) {
-            if (in) {
-                pv[st] = *reinterpret_cast<const bf16x8*>(src + 16 * st);
+            for (int st = 0; st < DR / 16; ++st) {
+                if (in) {
+                    pv.p[st] = *reinterpret_cast<const bf16x8*>(src + 16 * st);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pv.p[st][i] = (__bf16)0.f;
+                }
+            }
+        } else {
+            const int d0 = C.w_lo - jb - 32;
+            const int d = d0 + 4 * (lane & 7);
+            // wave-uniform: every column real and every distance in [0, R)
+            if (!C.phantom && d0 >= 0 && d0 + 31 < A.R) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const f32x4u v = *reinterpret_cast<const f32x4u*>(relc + 8 * k * rel_rs + d);
+                    pv.p[k] = f32x4{v[0], v[1], v[2], v[3]};
+                }
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pv[st][i] = (__bf16)0.f;
+                for (int k = 0; k < 4; ++k) {
+                    const bool col = 8 * k + (lane >> 3) <= qb - qa;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool in = col && (unsigned)(d + i) < (unsigned)A.R;
+                        pv.p[k][i] = in ? relc[8 * k * rel_rs + d + i] : 0.f;
+                    }
+                }
             }
         }
     };
@@ -994,9 +1009,9 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
     // bands' projection rows, the block-table slice) behind a single wait,
     // then the first copy, then the first two bands; so one HBM round trip
     // precedes the copy instead of a chain of them.
-    bf16x8 rreg[DR / 16];  // r of the lane's column: the band's B operand
-    bf16x8 pv[DR / 16];    // projection rows of the next band
-    bf16x8 pv0[DR / 16];   // (start only) rows of the band before the first
+    bf16x8 rreg[DR > 0 ? DR / 16 : 1];  // r of the lane's column: the band's B operand
+    BandSrc<DR> pv;                      // sources of the next band
+    BandSrc<DR> pv0;                     // (start only) sources of the band before the first
     const bool band_first = rel_active(js_lo);
     if (band_first) {
         load_p(pv0, js_lo - 32);
@@ -1048,20 +1063,31 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
             vbo[dt] = vr * DV + 32 * ((dt + vrot<DV>(vr)) & (DV / 32 - 1)) + 16 * (gq & 1) + 4 * (j & 3);
     }
 
-    // T(jb) from the rows p into the ring: lane (n, hh) holds rows 8 i + 4 hh + 0..3
-    auto band = [&](const bf16x8 (&p)[DR / 16], int jb) {
-        f32x16 Tb = zero16();
-#pragma unroll
-        for (int st = 0; st < DR / 16; ++st) Tb = mfma32(p[st], rreg[st], Tb);
+    // T(jb) into the ring. DR > 0: from the rows p, lane (n, hh) holding
+    // rows 8 i + 4 hh + 0..3 of column n. DR = 0: the rel pieces as loaded.
+    auto band = [&](const BandSrc<DR>& p, int jb) {
         const int par = (jb >> 5) & 1;
+        if constexpr (DR > 0) {
+            f32x16 Tb = zero16();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 v = {Tb[4 * i], Tb[4 * i + 1], Tb[4 * i + 2], Tb[4 * i + 3]};
-            *reinterpret_cast<f32x4*>(ring + 32 * par + 8 * i + 4 * hh) = v;
-        }
-        if (par == 0) {
-            const f32x4 v = {Tb[0], Tb[1], Tb[2], Tb[3]};
-            *reinterpret_cast<f32x4*>(ring + 64 + 4 * hh) = v;
+            for (int st = 0; st < DR / 16; ++st) Tb = mfma32(p.p[st], rreg[st], Tb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = {Tb[4 * i], Tb[4 * i + 1], Tb[4 * i + 2], Tb[4 * i + 3]};
+                *reinterpret_cast<f32x4*>(ring + 32 * par + 8 * i + 4 * hh) = v;
+            }
+            if (par == 0) {
+                const f32x4 v = {Tb[0], Tb[1], Tb[2], Tb[3]};
+                *reinterpret_cast<f32x4*>(ring + 64 + 4 * hh) = v;
+            }
+        } else {
+            const int q = lane & 7;
+            float* dst = ring_all + wid * 32 * RSTRIDE + (lane >> 3) * RSTRIDE + 4 * q;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                *reinterpret_cast<f32x4*>(dst + 8 * k * RSTRIDE + 32 * par) = p.p[k];
+                if (par == 0 && q < 2) *reinterpret_cast<f32x4*>(dst + 8 * k * RSTRIDE + 64) = p.p[k];
+            }
         }
     };
     // bias of subtile js in the score layout (register 8 c + e: key
@@ -1184,22 +1210,43 @@ __device__ __forceinline__ void prefill_relproj_body(const PrefillArgs A) {
 
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, false, DR>(A);
+    prefill_ring_body<DV, false, DR>(A);
 }
 
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_logpos_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, true, DR>(A);
+    prefill_ring_body<DV, true, DR>(A);
 }
 
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_fp8_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, false, DR, true>(A);
+    prefill_ring_body<DV, false, DR, true>(A);
 }
 
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_fp8_logpos_kernel(const PrefillArgs A) {
-    prefill_relproj_body<DV, true, DR, true>(A);
+    prefill_ring_body<DV, true, DR, true>(A);
+}
+
+// Windowed prefill over a materialised rel, the bias staged through the ring.
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_ring_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, 0>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_ring_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, 0>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_ring_fp8_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, 0, true>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_ring_fp8_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, 0, true>(A);
 }
 
 // ---------------------------------------------------------------------------
@@ -2274,31 +2321,42 @@ __global__ void __launch_bounds__(256) rel_rows_kernel(const RelRowsArgs A) {
 
 namespace {
 
-template <int DV, bool WIN>
+template <int DV>
 void launch_prefill_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
     if (a.kv8) {
-        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV, WIN>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_fp8_kernel<DV, WIN>), g, blk, 0, s, a);
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_fp8_kernel<DV>), g, blk, 0, s, a);
     } else {
-        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_logpos_kernel<DV, WIN>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<DV, WIN>), g, blk, 0, s, a);
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_kernel<DV>), g, blk, 0, s, a);
+    }
+}
+
+template <int DV>
+void launch_ring_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.kv8) {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_ring_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_ring_fp8_kernel<DV>), g, blk, 0, s, a);
+    } else {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_ring_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_ring_kernel<DV>), g, blk, 0, s, a);
     }
 }
 
 }  // namespace
 
-// Kernel choice: windowed (every subtile streams bias) or not; per-row logit
-// scale or not; bf16 or e4m3 K/V.
+// Kernel choice: windowed (every subtile streams bias: the ring kernel) or
+// not; per-row logit scale or not; bf16 or e4m3 K/V.
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
     const dim3 g((unsigned)grid), blk(512);
     if (a.W > 0) {
-        if (dv == 128) launch_prefill_t<128, true>(a, g, blk, s);
-        else launch_prefill_t<64, true>(a, g, blk, s);
+        if (dv == 128) launch_ring_t<128>(a, g, blk, s);
+        else launch_ring_t<64>(a, g, blk, s);
     } else {
-        if (dv == 128) launch_prefill_t<128, false>(a, g, blk, s);
-        else launch_prefill_t<64, false>(a, g, blk, s);
+        if (dv == 128) launch_prefill_t<128>(a, g, blk, s);
+        else launch_prefill_t<64>(a, g, blk, s);
     }
     return hipGetLastError();
 }

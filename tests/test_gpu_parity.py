@@ -348,11 +348,11 @@ def test_chunked_prefill_is_bitwise_equal_to_one_shot():
 
 
 def test_windowed_chunked_prefill_within_the_bf16_p_bound():
-    """With a window, a tile walks its blocks as a rotation that depends on the
-    tile's alignment, so a chunked call visits a row's keys in another order
-    than the one-shot call and rounds P against other running references:
-    the two agree element by element within the bf16-P bound (2^-8 E_p|v|),
-    not bitwise."""
+    """With a window, a tile starts at the first 64-key stage that any of its
+    rows can see. A chunk's tiles start at other rows than the one-shot
+    call's, so a row's keys may be visited from another first stage and P
+    rounded against other running references: the two agree element by
+    element within the bf16-P bound (2^-8 E_p|v|), not bitwise."""
     say("chunking, windowed")
     full_cpu = W.make_prefill(6, [640], [0], 8, 2, 128, 256, 300)
     full = full_cpu.to(DEV)
