@@ -56,7 +56,7 @@ LEGS = [
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILES = {
     "decode": os.path.join(PROFILES, "decode16_split_kernel_paged_decode_16_disjoint_traffic.txt"),
-    "global_prefill": os.path.join(PROFILES, "prefill_kernel_global_chunked_prefill_32k_traffic.txt"),
+    "global_prefill": os.path.join(PROFILES, "prefill_tail_kernel_global_chunked_prefill_32k_traffic.txt"),
 }
 CSRC = os.path.join(ROOT, "relative_position_bias_amd", "csrc")
 KERNEL_SRCS = [os.path.join(CSRC, "rba_kernels.hip"), os.path.join(CSRC, "rba_internal.h")]
@@ -432,7 +432,7 @@ def main():
         t = sum(ms[k] for k in ks) / 1e3
         f = sum(calls[k][3] for k in ks)
         nb = sum(calls[k][4] for k in ks)
-        kname = f"prefill_ring_kernel<{b.dv}>" if b.W > 0 else f"prefill_kernel<{b.dv}>"
+        kname = f"prefill_ring_kernel<{b.dv}>" if b.W > 0 else f"prefill_tail_kernel<{b.dv}>"
         if f / PEAK_MFMA_BF16 >= nb / PEAK_HBM:
             achieved = f / t / 1e12
             blk = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),

@@ -26,10 +26,10 @@
 //     transposed writes.
 //   * The bias is "sheared": element (column n, key j) needs rel[t_n, h_n,
 //     i_n - j], and a lane's 8 consecutive keys are 8 consecutive (falling)
-//     distances of its own rel row. The prefill without a window loads them
-//     straight into registers (two 16-byte loads per run); the windowed
-//     prefill stages them through a per-column LDS ring (below); the decode
-//     loads, with 16-byte
+//     distances of its own rel row. The prefill stages them through a
+//     per-column LDS ring (below), except over e4m3 K/V without a window,
+//     where each lane loads them straight into registers (two 16-byte loads
+//     per run); the decode loads, with 16-byte
 //     loads, the aligned superset of its 32 rel row segments (32 rows x 36
 //     floats), parks it in an LDS band and reads every lane's 16 values back
 //     along the shear. Subtiles whose distances are all >= R skip rel
@@ -42,14 +42,15 @@
 //   * Prefill: a workgroup of 8 waves shares each 128-key K/V block in LDS for
 //     up to 8 query heads of one KV head (GQA packing) and 32..256 query rows.
 //     Blocks are copied HBM -> LDS by global_load_lds into double buffers
-//     (one barrier per block); the next subtile's bias comes straight into
-//     registers. The block-table slice sits in a register (one entry per
-//     lane) so no load waits on a table read.
-//   * Windowed prefill, where every subtile carries bias: each wave keeps the
-//     last two 32-distance bands of its columns' rel rows in a per-column
-//     LDS ring, loaded 128 bytes of a row per 8 lanes, and reads each lane's
-//     values back along the shear. The ring leaves room for half-block K/V
-//     stages only.
+//     (one barrier per block). The block-table slice sits in a register (one
+//     entry per lane) so no load waits on a table read.
+//   * Bias in the prefill: from the first 64-key stage that carries bias for
+//     any row of the tile on (every stage with a window; the last ~R keys
+//     without one), each wave keeps the last two 32-distance bands of its
+//     columns' rel rows in a per-column LDS ring, loaded 128 bytes of a row
+//     per 8 lanes, and reads each lane's values back along the shear. The
+//     ring leaves room for half-block K/V stages only, so the blocks before
+//     that point go whole and the rest in halves.
 //   * Prefill with the bias made in the kernel (rel = r @ rel_logits_proj,
 //     "Attention with a relative bias"): each wave forms the 63-distance band
 //     of a subtile from r (an MFMA operand held for the whole sweep) and the
@@ -656,8 +657,8 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
 // single pair of bf16 buffers K0 / V0 between two barriers; the compute loop
 // is the bf16 one. The K scale is folded into c1, the V scale into the
 // output.
-// Windowed calls go to prefill_ring_body; the tile logic here still covers
-// any window.
+// This body runs the prefill without a window over e4m3 K/V (the other
+// prefill calls go to prefill_ring_body); its tile logic covers any window.
 template <int DV, bool LS, bool KV8 = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
     constexpr int NW = 4;  // waves that issue the K/V copies
@@ -825,16 +826,6 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs A) {
 }
 
 template <int DV>
-__global__ void __launch_bounds__(512) prefill_kernel(const PrefillArgs A) {
-    prefill_body<DV, false>(A);
-}
-
-template <int DV>
-__global__ void __launch_bounds__(512) prefill_logpos_kernel(const PrefillArgs A) {
-    prefill_body<DV, true>(A);
-}
-
-template <int DV>
 __global__ void __launch_bounds__(512) prefill_fp8_kernel(const PrefillArgs A) {
     prefill_body<DV, false, true>(A);
 }
@@ -892,19 +883,31 @@ struct BandSrc<0> {
 // DR: the width of r (32, 64 or 128), or 0 for a materialised rel. KV8: e4m3
 // K/V caches, staged and widened per stage as in prefill_body (one pair of
 // bf16 stage buffers).
-template <int DV, bool LS, int DR, bool KV8 = false>
+//
+// WB (no window, bf16 K/V): the blocks before the first subtile that carries
+// bias for any row of the tile are walked whole, as prefill_body walks them
+// (double-buffered 128-key blocks, no bias); the ring and the half-block
+// stages take over from the first block with bias. The whole blocks
+// alternate between the two buffers so that the last one is in buffer 1,
+// which then holds the rings (with the LDS after it); buffer 0 holds the
+// stages.
+template <int DV, bool LS, int DR, bool KV8 = false, bool WB = false>
 __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
-    constexpr int NW = 8;   // every wave issues copies
+    static_assert(!(WB && KV8), "whole blocks first: bf16 K/V only");
+    constexpr int NW = 8;   // every wave issues stage copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
-    __shared__ __attribute__((aligned(16))) __bf16 K0[HB * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 ? 8 : HB * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 V0[HB * DV];
-    __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 ? 8 : HB * DV];
+    constexpr int RING_W = 32 * RSTRIDE;                   // floats of one wave's ring
+    constexpr int BLK = BS * (DQK + DV);                   // bf16 of one whole K/V block
+    constexpr int RINGS_P = (2 * BLK) / (4 * RING_W);      // rings in one whole-block buffer
+    __shared__ __attribute__((aligned(16))) __bf16 K0[WB ? 8 : HB * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 || WB ? 8 : HB * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 V0[WB ? 8 : HB * DV];
+    __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 || WB ? 8 : HB * DV];
     __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 ? HB * (DQK + DV) : 16];
-    __shared__ __attribute__((aligned(16))) float ring_all[8 * 32 * RSTRIDE];
-    __bf16* const KB = KV8 ? K0 : K1;
-    __bf16* const VB = KV8 ? V0 : V1;
+    __shared__ __attribute__((aligned(16))) float ring_all[WB ? 4 : 8 * RING_W];
+    // WB: two whole-block buffers, then the rings that do not fit in one
+    __shared__ __attribute__((aligned(16))) __bf16 WBUF[WB ? 2 * BLK + 2 * (8 - RINGS_P) * RING_W : 8];
     const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(A.k);
     const uint8_t* const v8 = reinterpret_cast<const uint8_t*>(A.v);
 
@@ -947,18 +950,32 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     C.w_hi = ctx + qb;
     C.phantom = qb < qa + 31;
     const uint16_t* proj = DR > 0 ? A.proj + (size_t)(A.proj_heads == A.Hq ? h : 0) * A.R * DR : nullptr;
-    float* ring = ring_all + wid * 32 * RSTRIDE + n * RSTRIDE;  // this lane's column
-    // DR = 0: rel row of column lane >> 3 (the loads of band pieces add 8 k rows)
+    // stage buffers and this wave's ring (WB: set where the ring phase starts)
+    __bf16 *Ks0 = K0, *Vs0 = V0, *Ks1 = KV8 ? K0 : K1, *Vs1 = KV8 ? V0 : V1;
+    float* ringw = ring_all + wid * RING_W;
+    float* ring = ringw + n * RSTRIDE;  // this lane's column
+    // DR = 0: rel row of the wave's first column (band pieces add the rows of
+    // columns (lane >> 3) + 8 k)
     const long long rel_rs = (long long)A.Hq * A.R;
-    const float* relc = DR == 0 && wave_active
-                            ? A.rel + ((long long)(q_start + qa) * A.Hq + h) * A.R + (lane >> 3) * rel_rs
-                            : nullptr;
+    const float* rel0 = DR == 0 && wave_active ? A.rel + ((long long)(q_start + qa) * A.Hq + h) * A.R : nullptr;
 
     const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
     const int s_lo = (A.W > 0 ? max(0, i_lo - A.W + 1) : 0) / HB;
     const int s_hi = i_hi / HB;
-    const int js_lo = s_lo * HB;
     const int kb_lo = s_lo / SPB, kb_hi = s_hi / SPB;
+    // WB: whole blocks kb_lo .. kb_sw - 1, then stages from s_first. A
+    // subtile js carries bias for the tile's first row i_lo (and so for no
+    // row at all before it) iff i_lo - (js + 31) < R.
+    int kb_sw = kb_lo;
+    if constexpr (WB) {
+        const int t = i_lo - 31 - A.R;
+        const int js_b = t < 0 ? 0 : (t / 32 + 1) * 32;
+        kb_sw = min(max(js_b / BS, kb_lo), kb_hi + 1);
+    }
+    const int n1 = kb_sw - kb_lo;          // whole blocks
+    const int s_first = WB ? kb_sw * SPB : s_lo;
+    const int js_lo = s_first * HB;        // first key of the ring phase
+    const bool ring_phase = s_first <= s_hi;
     const int* tab = A.tables + (long long)b * A.max_blocks;
 
     auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
@@ -982,6 +999,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
                 }
             }
         } else {
+            const float* relc = rel0 + (lane >> 3) * rel_rs;
             const int d0 = C.w_lo - jb - 32;
             const int d = d0 + 4 * (lane & 7);
             // wave-uniform: every column real and every distance in [0, R)
@@ -1012,7 +1030,9 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     bf16x8 rreg[DR > 0 ? DR / 16 : 1];  // r of the lane's column: the band's B operand
     BandSrc<DR> pv;                      // sources of the next band
     BandSrc<DR> pv0;                     // (start only) sources of the band before the first
-    const bool band_first = rel_active(js_lo);
+    // WB with whole blocks first: the first bands' sources are requested
+    // after the last whole block instead.
+    bool band_first = n1 == 0 && ring_phase && rel_active(js_lo);
     if (band_first) {
         load_p(pv0, js_lo - 32);
         load_p(pv, js_lo);
@@ -1082,7 +1102,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
             }
         } else {
             const int q = lane & 7;
-            float* dst = ring_all + wid * 32 * RSTRIDE + (lane >> 3) * RSTRIDE + 4 * q;
+            float* dst = ringw + (lane >> 3) * RSTRIDE + 4 * q;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 *reinterpret_cast<f32x4*>(dst + 8 * k * RSTRIDE + 32 * par) = p.p[k];
@@ -1123,16 +1143,70 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     };
 
     bool ok = false;
-    {
-        const size_t row = stage_row(s_lo, ok);
+    if constexpr (WB) {
+        Ks0 = WBUF;
+        Vs0 = Ks0 + HB * DQK;
+        Ks1 = Vs0 + HB * DV;
+        Vs1 = Ks1 + HB * DQK;
+        ringw = reinterpret_cast<float*>(WBUF + BLK) + wid * RING_W;
+        ring = ringw + n * RSTRIDE;
+    }
+    if (WB && n1 > 0) {
+        __bf16* K1st = WBUF + (n1 & 1) * BLK;  // whole block i goes to buffer (i + n1) mod 2
+        const size_t row = stage_row(kb_lo * SPB, ok);
+        if (ok) kv_dma<DV, 4>(K1st, K1st + BS * DQK, A.k + row * DQK, A.v + row * DV, L - kb_lo * BS, wid, lane);
+    } else if (ring_phase) {
+        const size_t row = stage_row(s_first, ok);
         if constexpr (KV8) {
             if (ok) kv8_dma<DV, NW, HB>(S8, k8 + row * DQK, v8 + row * DV, wid, lane);
         } else {
-            if (ok) kv_dma<DV, NW, HB>(K0, V0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
+            if (ok) kv_dma<DV, NW, HB>(Ks0, Vs0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
         }
     }
     int band_js = INT_MIN;  // last band in the ring
     int pv_js = INT_MIN;    // band whose projection rows pv holds
+
+    // WB: the whole blocks (no row of the tile has bias there). The last one
+    // starts the ring phase's first copy into the other buffer; the first two
+    // bands' sources are requested after it.
+    if constexpr (WB) {
+#pragma unroll 1
+        for (int i = 0; i < n1; ++i) {
+            const int kb = kb_lo + i;
+            const __bf16* Kc = WBUF + ((i + n1) & 1) * BLK;
+            const __bf16* Vc = Kc + BS * DQK;
+            __bf16* Kn = WBUF + ((i + 1 + n1) & 1) * BLK;
+            vm_wait_all();
+            lds_barrier();
+            const bool ok_cur = ok;
+            bad = bad || !ok_cur;
+            if (i + 1 < n1) {
+                const size_t row = stage_row((kb + 1) * SPB, ok);
+                if (ok) kv_dma<DV, 4>(Kn, Kn + BS * DQK, A.k + row * DQK, A.v + row * DV, L - (kb + 1) * BS, wid, lane);
+            } else if (ring_phase) {
+                const size_t row = stage_row(s_first, ok);
+                if (ok) kv_dma<DV, NW, HB>(Ks0, Vs0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
+            }
+            if (wave_active && ok_cur) {
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub) {
+                    const int js = kb * BS + 32 * sub;
+                    if (!masked_all(C, js, A.W)) compute(Kc, Vc, sub, js, false);
+                }
+            }
+        }
+        if (n1 > 0 && ring_phase) {
+            // (requested only now, so that they are not live across the last
+            // whole block's compute)
+            if (rel_active(js_lo)) {
+                load_p(pv0, js_lo - 32);
+                load_p(pv, js_lo);
+                band_first = true;
+            }
+            vm_wait_all();
+            lds_barrier();  // every wave is done with the buffer that becomes the rings
+        }
+    }
     if (band_first) {
         band(pv0, js_lo - 32);
         band(pv, js_lo);
@@ -1196,10 +1270,10 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         }
         if (comp1) compute(Kc, Vc, 1, js1, bias1);
     };
-    for (int s = s_lo;;) {
-        step(K0, V0, KB, VB, s);
+    for (int s = s_first; ring_phase;) {
+        step(Ks0, Vs0, Ks1, Vs1, s);
         if (++s > s_hi) break;
-        step(KB, VB, K0, V0, s);
+        step(Ks1, Vs1, Ks0, Vs0, s);
         if (++s > s_hi) break;
     }
 
@@ -1232,6 +1306,28 @@ __global__ void __launch_bounds__(512) prefill_relproj_fp8_logpos_kernel(const P
 template <int DV>
 __global__ void __launch_bounds__(512) prefill_ring_kernel(const PrefillArgs A) {
     prefill_ring_body<DV, false, 0>(A);
+}
+
+// Prefill without a window: whole blocks, then the ring from the first block with bias.
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_tail_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, 0, false, true>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_tail_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, 0, false, true>(A);
+}
+
+// The same with the bias made in the kernel.
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_tail_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, DR, false, true>(A);
+}
+
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_tail_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, DR, false, true>(A);
 }
 
 template <int DV>
@@ -2322,14 +2418,15 @@ __global__ void __launch_bounds__(256) rel_rows_kernel(const RelRowsArgs A) {
 namespace {
 
 template <int DV>
-void launch_prefill_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.kv8) {
-        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_fp8_kernel<DV>), g, blk, 0, s, a);
-    } else {
-        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_logpos_kernel<DV>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<DV>), g, blk, 0, s, a);
-    }
+void launch_prefill_fp8_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prefill_fp8_kernel<DV>), g, blk, 0, s, a);
+}
+
+template <int DV>
+void launch_tail_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
+    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_tail_logpos_kernel<DV>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prefill_tail_kernel<DV>), g, blk, 0, s, a);
 }
 
 template <int DV>
@@ -2346,7 +2443,8 @@ void launch_ring_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
 }  // namespace
 
 // Kernel choice: windowed (every subtile streams bias: the ring kernel) or
-// not; per-row logit scale or not; bf16 or e4m3 K/V.
+// not (bf16 K/V: whole blocks, then the ring; e4m3 K/V: whole blocks with
+// the bias loaded per lane); per-row logit scale or not.
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
@@ -2354,9 +2452,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     if (a.W > 0) {
         if (dv == 128) launch_ring_t<128>(a, g, blk, s);
         else launch_ring_t<64>(a, g, blk, s);
+    } else if (!a.kv8) {
+        if (dv == 128) launch_tail_t<128>(a, g, blk, s);
+        else launch_tail_t<64>(a, g, blk, s);
     } else {
-        if (dv == 128) launch_prefill_t<128>(a, g, blk, s);
-        else launch_prefill_t<64>(a, g, blk, s);
+        if (dv == 128) launch_prefill_fp8_t<128>(a, g, blk, s);
+        else launch_prefill_fp8_t<64>(a, g, blk, s);
     }
     return hipGetLastError();
 }
@@ -2365,7 +2466,10 @@ namespace {
 
 template <int DV, int DR>
 void launch_relproj_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.kv8) {
+    if (a.W == 0 && !a.kv8) {  // whole blocks until the first block with bias
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_tail_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_relproj_tail_kernel<DV, DR>), g, blk, 0, s, a);
+    } else if (a.kv8) {
         if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_fp8_logpos_kernel<DV, DR>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((prefill_relproj_fp8_kernel<DV, DR>), g, blk, 0, s, a);
     } else {

@@ -80,10 +80,9 @@ def test_relproj_other_r_widths(case, d_r):
 def test_relproj_equals_materialised_bias(case):
     """The same call through rba_prefill with rel formed by the oracle
     (float64, rounded to fp32): the two calls visit the keys in the same
-    order (with a window both run the ring kernel and differ only in where
-    its bands come from; without one, rba_prefill's whole blocks hold the
-    same 32-key subtiles in the same ascending order), so they differ only
-    by the fp32 rounding of the bias. Element by element they must agree
+    order (both run the ring body, with or without whole blocks before the
+    first block with bias, and differ only in where its bands come from), so
+    they differ only by the fp32 rounding of the bias. Element by element they must agree
     within the bf16-P bound (a rounding of some P that the bias difference
     flips costs at most 2^-9 of that weight: |o1 - o2| <= 2^-8 E_p|v|
     + 1e-5, E_p|v| the softmax-weighted mean of |v| from the oracle on |V|),
