@@ -27,9 +27,7 @@
 //   * The bias is "sheared": element (column n, key j) needs rel[t_n, h_n,
 //     i_n - j], and a lane's 8 consecutive keys are 8 consecutive (falling)
 //     distances of its own rel row. The prefill stages them through a
-//     per-column LDS ring (below), except over e4m3 K/V without a window,
-//     where each lane loads them straight into registers (two 16-byte loads
-//     per run); the decode loads, with 16-byte
+//     per-column LDS ring (below); the decode loads, with 16-byte
 //     loads, the aligned superset of its 32 rel row segments (32 rows x 36
 //     floats), parks it in an LDS band and reads every lane's 16 values back
 //     along the shear. Subtiles whose distances are all >= R skip rel
@@ -650,191 +648,6 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
     return halves_max(M);
 }
 
-// LS: each query row's logits are multiplied by A.lscale[row] (the
-// log-position scale of global layers, "What was built"); otherwise by 1.
-// KV8: e4m3 K/V caches. Each block is copied as bytes into S8 (the copy of
-// the next block overlaps the current block's compute) and widened into a
-// single pair of bf16 buffers K0 / V0 between two barriers; the compute loop
-// is the bf16 one. The K scale is folded into c1, the V scale into the
-// output.
-// This body runs the prefill without a window over e4m3 K/V (the other
-// prefill calls go to prefill_ring_body); its tile logic covers any window.
-template <int DV, bool LS, bool KV8 = false>
-__device__ __forceinline__ void prefill_body(const PrefillArgs A) {
-    constexpr int NW = 4;  // waves that issue the K/V copies
-    __shared__ __attribute__((aligned(16))) __bf16 K0[BS * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 ? 8 : BS * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 V0[BS * DV];
-    __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 ? 8 : BS * DV];
-    __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 ? BS * (DQK + DV) : 16];
-    __bf16* const KB = KV8 ? K0 : K1;  // the second buffer pair (the first one again for e4m3)
-    __bf16* const VB = KV8 ? V0 : V1;
-    const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(A.k);
-    const uint8_t* const v8 = reinterpret_cast<const uint8_t*>(A.v);
-
-    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
-    int id = blockIdx.x;
-    const int g = id % A.Hkv;
-    id /= A.Hkv;
-    const int b = id % A.batch;
-    id /= A.batch;
-    const int hc = id % A.n_hc;
-    id /= A.n_hc;
-    // The late tiles (more keys) go first.
-    const int qt = A.n_qt - 1 - id;
-
-    const int q_start = A.cu_q[b];
-    const int q_len = A.cu_q[b + 1] - q_start;
-    const int L = A.seq_lens[b];
-    const int q0 = qt * A.QT;
-    if (q0 >= q_len) return;  // uniform over the workgroup
-    const int ctx = L - q_len;
-
-    const int hl = hc * A.hpw + wid % A.hpw;
-    const int h = g * A.G + hl;
-    const int qa = q0 + (wid / A.hpw) * 32;
-    const int qb = min(qa + 32, q_len) - 1;
-    const bool wave_active = qa < q_len;
-    const int r = qa + n;
-    const bool real = r < q_len;
-    const long long trow = (long long)(q_start + (real ? r : 0)) * A.Hq + h;
-    const float fls = (LS && real) ? A.lscale[q_start + r] : 1.f;  // the row's logit scale
-    const float c1f = A.c1 * fls, l2f = LOG2E * fls;
-
-    Cols<DV> C;
-    C.pos = real ? ctx + r : -1;
-    C.relrow = A.rel + trow * A.R;
-    C.w_lo = ctx + qa;
-    C.w_hi = ctx + qb;
-    C.phantom = qb < qa + 31;
-    load_q(C, A.q + trow * DQK, lane);
-    init_acc(C);
-    // A device length that breaks the caller's contract (fewer keys than new
-    // rows, or more keys than the block-table row can address) makes the
-    // tile's rows NaN; no table entry past the row is ever read.
-    if (ctx < 0 || (long long)L > (long long)A.max_blocks * BS) {
-        if (wave_active && real)
-            store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, true, -INFINITY, INFINITY, lane);
-        return;
-    }
-
-    const int i_lo = ctx + q0, i_hi = ctx + min(q0 + A.QT, q_len) - 1;
-    const int kb_lo = A.W > 0 ? max(0, i_lo - A.W + 1) / BS : 0;
-    const int kb_hi = i_hi / BS;
-    const int* tab = A.tables + (long long)b * A.max_blocks;
-    bool bad = false;
-
-    // block-table slice of the tile (lane i = entry tab_base + i)
-    int tab_base = kb_lo;
-    int tabv = (kb_lo + lane <= kb_hi) ? tab[kb_lo + lane] : -1;
-    auto block_base = [&](int kb, bool& okk) -> size_t {
-        if (kb - tab_base >= 64) {
-            tab_base += 64;
-            tabv = (tab_base + lane <= kb_hi) ? tab[tab_base + lane] : -1;
-        }
-        const int phys = __builtin_amdgcn_readlane(tabv, kb - tab_base);
-        okk = phys >= 0 && phys < A.num_blocks;
-        return okk ? ((size_t)phys * A.Hkv + g) * BS : 0;
-    };
-
-    auto rel_active = [&](int js) { return wave_active && !masked_all(C, js, A.W) && bias_on(C, js, A.R); };
-    auto rel_inside = [&](int js) { return !C.phantom && C.w_lo - js - 31 >= 0 && C.w_hi - js < A.R; };
-
-    int koff[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) koff[st] = n * DQK + 8 * ((2 * st + (lane >> 5)) ^ (n & 15));
-    // lane offsets of the transposed V reads, one per 32-dim tile: row
-    // 8 (g >> 1) + (j >> 2) of the 16-key chunk, dims 32 dt + 16 (g & 1) + 4 (j & 3)
-    int vbo[DV / 32];
-    {
-        const int gq = lane >> 4, j = lane & 15, vr = 8 * (gq >> 1) + (j >> 2);
-#pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt)
-            vbo[dt] = vr * DV + 32 * ((dt + vrot<DV>(vr)) & (DV / 32 - 1)) + 16 * (gq & 1) + 4 * (j & 3);
-    }
-
-    bool ok = false;
-    {
-        const size_t base = block_base(kb_lo, ok);
-        if constexpr (KV8) {
-            if (ok) kv8_dma<DV, NW>(S8, k8 + base * DQK, v8 + base * DV, wid, lane);
-        } else {
-            if (ok) kv_dma<DV, NW>(K0, V0, A.k + base * DQK, A.v + base * DV, L - kb_lo * BS, wid, lane);
-        }
-    }
-    RelVals rv[2];  // bias of the current and of the next subtile
-    if (rel_active(kb_lo * BS)) rel_fetch(rv[0], C.relrow, C.pos, kb_lo * BS, A.R, rel_inside(kb_lo * BS), lane);
-
-    // One block: wait for its copy, start the next block's copy into the
-    // other buffers (every wave left them at this barrier), compute.
-    auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn, int kb) {
-        vm_wait_all();
-        lds_barrier();
-        const bool ok_cur = ok;
-        bad = bad || !ok_cur;
-        const int kbn = kb != kb_hi ? kb + 1 : -1;  // the next block, if any
-        if constexpr (KV8) {
-            kv8_widen<DV>(K0, V0, S8, L - kb * BS, tid);  // this block, bytes -> bf16
-            lds_barrier();                                 // widened block visible, S8 free
-            if (kbn >= 0) {
-                const size_t base = block_base(kbn, ok);
-                if (ok) kv8_dma<DV, NW>(S8, k8 + base * DQK, v8 + base * DV, wid, lane);
-            }
-        } else if (kbn >= 0) {
-            const size_t base = block_base(kbn, ok);
-            if (ok) kv_dma<DV, NW>(Kn, Vn, A.k + base * DQK, A.v + base * DV, L - kbn * BS, wid, lane);
-        }
-        if (!wave_active) return;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            const int js = kb * BS + 32 * sub;
-            // The next subtile's bias is requested before this subtile's
-            // scores.
-            const int jn = sub < 3 ? js + 32 : (kbn >= 0 ? kbn * BS : -1);  // the next subtile
-            if (jn >= 0 && rel_active(jn))
-                rel_fetch(rv[(sub + 1) & 1], C.relrow, C.pos, jn, A.R, rel_inside(jn), lane);
-            if (ok_cur && !masked_all(C, js, A.W)) {
-                const f32x16 sc = qk_swz(Kc + 32 * sub * DQK, koff, C.qreg);
-                float x[16];
-                float M = sm_scores_rv(C, sc, rel_active(js), rv[sub & 1], rel_inside(js), need_mask_of(C, js, A.W),
-                                       js, A.W, A.R, c1f, l2f, lane, x);
-                if (__any(!C.m_set || sm_trigger(C, M))) {
-                    if (__any(!C.m_set)) sm_init_ref(C, M, x);
-                    if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
-                }
-                bf16x8 pb[2];
-                sm_probs(C, x, pb);
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int dt = 0; dt < DV / 32; ++dt)
-                        C.O[dt] = mfma32(v_operand_rot(Vc + (32 * sub + 16 * c) * DV, vbo[dt], DV), pb[c], C.O[dt]);
-                }
-            }
-        }
-    };
-    for (int kb = kb_lo;;) {
-        step(K0, V0, KB, VB, kb);
-        if (++kb > kb_hi) break;
-        step(KB, VB, K0, V0, kb);
-        if (++kb > kb_hi) break;
-    }
-
-    if (!wave_active || !real) return;
-    store_out(C, A.out + trow * DV, A.lse ? A.lse + trow : nullptr, bad, A.sink ? A.sink[trow] : -INFINITY,
-              A.gate ? A.gate[trow] : INFINITY, lane, KV8 ? A.v_scale : 1.f);
-}
-
-template <int DV>
-__global__ void __launch_bounds__(512) prefill_fp8_kernel(const PrefillArgs A) {
-    prefill_body<DV, false, true>(A);
-}
-
-template <int DV>
-__global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillArgs A) {
-    prefill_body<DV, true, true>(A);
-}
-
 // ---------------------------------------------------------------------------
 // Prefill with the bias produced in the kernel (rel = r @ rel_logits_proj)
 //
@@ -858,14 +671,14 @@ __global__ void __launch_bounds__(512) prefill_fp8_logpos_kernel(const PrefillAr
 // double-buffered whole K/V blocks, so K/V move in half blocks of 64 keys
 // (two subtiles per barrier).
 //
-// The windowed prefill over a materialised rel uses the same ring (DR = 0):
-// band T(jb) is then the rel entries of the 32 distances (w_lo - jb) - 32 ..
+// The prefill over a materialised rel uses the same ring (DR = 0): band
+// T(jb) is then the rel entries of the 32 distances (w_lo - jb) - 32 ..
 // (w_lo - jb) - 1 of each column's row, which start at the same distance in
 // every row. Eight lanes load one row's 128 bytes, so one load instruction
 // covers 8 rows; loading each lane's own 8-distance runs straight from HBM
-// (as prefill_body does) spreads every instruction over 32 rows, and on the
-// windowed prefill, where every subtile streams bias, the vector memory path
-// then saturates on the number of rows in flight.
+// instead spreads every instruction over 32 rows, and where every subtile
+// streams bias the vector memory path then saturates on the number of rows
+// in flight.
 // ---------------------------------------------------------------------------
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
@@ -880,34 +693,43 @@ struct BandSrc<0> {
     f32x4 p[4];
 };
 
-// DR: the width of r (32, 64 or 128), or 0 for a materialised rel. KV8: e4m3
-// K/V caches, staged and widened per stage as in prefill_body (one pair of
-// bf16 stage buffers).
+// DR: the width of r (32, 64 or 128), or 0 for a materialised rel. LS: each
+// query row's logits are multiplied by A.lscale[row] (the log-position scale
+// of global layers, "What was built"); otherwise by 1. KV8: e4m3 K/V caches:
+// each stage's (or whole block's) bytes are copied into a staging area of
+// LDS, the copy of the next one overlapping the current compute, and widened
+// between two barriers into a single pair of bf16 buffers; the compute loop
+// is the bf16 one. The K scale is folded into c1, the V scale into the
+// output.
 //
-// WB (no window, bf16 K/V): the blocks before the first subtile that carries
-// bias for any row of the tile are walked whole, as prefill_body walks them
-// (double-buffered 128-key blocks, no bias); the ring and the half-block
-// stages take over from the first block with bias. The whole blocks
-// alternate between the two buffers so that the last one is in buffer 1,
-// which then holds the rings (with the LDS after it); buffer 0 holds the
-// stages.
+// WB (no window): the blocks before the first subtile that carries bias for
+// any row of the tile are walked whole (128-key blocks, no bias code); the ring and the half-block stages take over from the
+// first block with bias. One LDS area is laid out twice. bf16 K/V: two
+// whole-block buffers, between which the whole blocks alternate so that the
+// last one is in buffer 1; the ring phase then puts its stages in buffer 0
+// and the rings in buffer 1 and the LDS after it. e4m3 K/V: one bf16
+// whole-block buffer and the byte staging area; the ring phase widens its
+// stages into the bottom of the buffer and puts three (dv 64: two) rings
+// above them, the others after the staging area.
 template <int DV, bool LS, int DR, bool KV8 = false, bool WB = false>
 __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
-    static_assert(!(WB && KV8), "whole blocks first: bf16 K/V only");
     constexpr int NW = 8;   // every wave issues stage copies
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
-    constexpr int RING_W = 32 * RSTRIDE;                   // floats of one wave's ring
-    constexpr int BLK = BS * (DQK + DV);                   // bf16 of one whole K/V block
-    constexpr int RINGS_P = (2 * BLK) / (4 * RING_W);      // rings in one whole-block buffer
+    constexpr int RING_W = 32 * RSTRIDE;        // floats of one wave's ring
+    constexpr int RINGB = 4 * RING_W;           // bytes of one wave's ring
+    constexpr int WHOLEB = 2 * BS * (DQK + DV); // bytes of a bf16 whole-block K/V pair
+    constexpr int HALFB = 2 * HB * (DQK + DV);  // bytes of a bf16 half-block K/V pair
+    constexpr int S8B = BS * (DQK + DV);        // bytes of an e4m3 whole block
+    constexpr int RINGS_IN = KV8 ? (WHOLEB - HALFB) / RINGB : WHOLEB / RINGB;  // rings inside the block area
+    constexpr int WB_BYTES = (KV8 ? WHOLEB + S8B : 2 * WHOLEB) + (8 - RINGS_IN) * RINGB;
     __shared__ __attribute__((aligned(16))) __bf16 K0[WB ? 8 : HB * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 K1[KV8 || WB ? 8 : HB * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 V0[WB ? 8 : HB * DV];
     __shared__ __attribute__((aligned(16))) __bf16 V1[KV8 || WB ? 8 : HB * DV];
-    __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 ? HB * (DQK + DV) : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t S8[KV8 && !WB ? HB * (DQK + DV) : 16];
     __shared__ __attribute__((aligned(16))) float ring_all[WB ? 4 : 8 * RING_W];
-    // WB: two whole-block buffers, then the rings that do not fit in one
-    __shared__ __attribute__((aligned(16))) __bf16 WBUF[WB ? 2 * BLK + 2 * (8 - RINGS_P) * RING_W : 8];
+    __shared__ __attribute__((aligned(16))) char WBL[WB ? WB_BYTES : 16];
     const uint8_t* const k8 = reinterpret_cast<const uint8_t*>(A.k);
     const uint8_t* const v8 = reinterpret_cast<const uint8_t*>(A.v);
 
@@ -950,8 +772,9 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     C.w_hi = ctx + qb;
     C.phantom = qb < qa + 31;
     const uint16_t* proj = DR > 0 ? A.proj + (size_t)(A.proj_heads == A.Hq ? h : 0) * A.R * DR : nullptr;
-    // stage buffers and this wave's ring (WB: set where the ring phase starts)
+    // stage buffers, e4m3 staging and this wave's ring (WB: set below)
     __bf16 *Ks0 = K0, *Vs0 = V0, *Ks1 = KV8 ? K0 : K1, *Vs1 = KV8 ? V0 : V1;
+    uint8_t* S8p = S8;
     float* ringw = ring_all + wid * RING_W;
     float* ring = ringw + n * RSTRIDE;  // this lane's column
     // DR = 0: rel row of the wave's first column (band pieces add the rows of
@@ -1143,22 +966,35 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     };
 
     bool ok = false;
+    __bf16* const Kw0 = reinterpret_cast<__bf16*>(WBL);  // WB: whole-block buffer 0
     if constexpr (WB) {
-        Ks0 = WBUF;
+        Ks0 = Kw0;
         Vs0 = Ks0 + HB * DQK;
-        Ks1 = Vs0 + HB * DV;
-        Vs1 = Ks1 + HB * DQK;
-        ringw = reinterpret_cast<float*>(WBUF + BLK) + wid * RING_W;
+        if constexpr (KV8) {
+            Ks1 = Ks0;
+            Vs1 = Vs0;
+            S8p = reinterpret_cast<uint8_t*>(WBL + WHOLEB);
+            ringw = wid < RINGS_IN ? reinterpret_cast<float*>(WBL + HALFB) + wid * RING_W
+                                   : reinterpret_cast<float*>(WBL + WHOLEB + S8B) + (wid - RINGS_IN) * RING_W;
+        } else {
+            Ks1 = Vs0 + HB * DV;
+            Vs1 = Ks1 + HB * DQK;
+            ringw = reinterpret_cast<float*>(WBL + WHOLEB) + wid * RING_W;
+        }
         ring = ringw + n * RSTRIDE;
     }
     if (WB && n1 > 0) {
-        __bf16* K1st = WBUF + (n1 & 1) * BLK;  // whole block i goes to buffer (i + n1) mod 2
         const size_t row = stage_row(kb_lo * SPB, ok);
-        if (ok) kv_dma<DV, 4>(K1st, K1st + BS * DQK, A.k + row * DQK, A.v + row * DV, L - kb_lo * BS, wid, lane);
+        if constexpr (KV8) {
+            if (ok) kv8_dma<DV, 4>(S8p, k8 + row * DQK, v8 + row * DV, wid, lane);
+        } else {
+            __bf16* K1st = Kw0 + (n1 & 1) * (WHOLEB / 2);  // whole block i goes to buffer (i + n1) mod 2
+            if (ok) kv_dma<DV, 4>(K1st, K1st + BS * DQK, A.k + row * DQK, A.v + row * DV, L - kb_lo * BS, wid, lane);
+        }
     } else if (ring_phase) {
         const size_t row = stage_row(s_first, ok);
         if constexpr (KV8) {
-            if (ok) kv8_dma<DV, NW, HB>(S8, k8 + row * DQK, v8 + row * DV, wid, lane);
+            if (ok) kv8_dma<DV, NW, HB>(S8p, k8 + row * DQK, v8 + row * DV, wid, lane);
         } else {
             if (ok) kv_dma<DV, NW, HB>(Ks0, Vs0, A.k + row * DQK, A.v + row * DV, L - js_lo, wid, lane);
         }
@@ -1173,14 +1009,24 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
 #pragma unroll 1
         for (int i = 0; i < n1; ++i) {
             const int kb = kb_lo + i;
-            const __bf16* Kc = WBUF + ((i + n1) & 1) * BLK;
+            const __bf16* Kc = KV8 ? Kw0 : Kw0 + ((i + n1) & 1) * (WHOLEB / 2);
             const __bf16* Vc = Kc + BS * DQK;
-            __bf16* Kn = WBUF + ((i + 1 + n1) & 1) * BLK;
+            __bf16* Kn = Kw0 + ((i + 1 + n1) & 1) * (WHOLEB / 2);
             vm_wait_all();
             lds_barrier();
             const bool ok_cur = ok;
             bad = bad || !ok_cur;
-            if (i + 1 < n1) {
+            if constexpr (KV8) {
+                kv8_widen<DV>(Kw0, Kw0 + BS * DQK, S8p, L - kb * BS, tid);  // this block, bytes -> bf16
+                lds_barrier();                                             // widened block visible, S8 free
+                if (i + 1 < n1) {
+                    const size_t row = stage_row((kb + 1) * SPB, ok);
+                    if (ok) kv8_dma<DV, 4>(S8p, k8 + row * DQK, v8 + row * DV, wid, lane);
+                } else if (ring_phase) {
+                    const size_t row = stage_row(s_first, ok);
+                    if (ok) kv8_dma<DV, NW, HB>(S8p, k8 + row * DQK, v8 + row * DV, wid, lane);
+                }
+            } else if (i + 1 < n1) {
                 const size_t row = stage_row((kb + 1) * SPB, ok);
                 if (ok) kv_dma<DV, 4>(Kn, Kn + BS * DQK, A.k + row * DQK, A.v + row * DV, L - (kb + 1) * BS, wid, lane);
             } else if (ring_phase) {
@@ -1223,7 +1069,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         bad = bad || !ok_cur;
         const int js0 = s * HB, js1 = js0 + 32;
         if constexpr (KV8) {
-            kv8_widen<DV, HB>(K0, V0, S8, L - js0, tid);  // this stage, bytes -> bf16
+            kv8_widen<DV, HB>(Ks0, Vs0, S8p, L - js0, tid);  // this stage, bytes -> bf16
             lds_barrier();                                 // widened stage visible, S8 free
         }
         const bool comp0 = wave_active && ok_cur && !masked_all(C, js0, A.W);
@@ -1243,7 +1089,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         if (s < s_hi) {
             const size_t row = stage_row(s + 1, ok);
             if constexpr (KV8) {
-                if (ok) kv8_dma<DV, NW, HB>(S8, k8 + row * DQK, v8 + row * DV, wid, lane);
+                if (ok) kv8_dma<DV, NW, HB>(S8p, k8 + row * DQK, v8 + row * DV, wid, lane);
             } else {
                 if (ok) kv_dma<DV, NW, HB>(Kn, Vn, A.k + row * DQK, A.v + row * DV, L - (s + 1) * HB, wid, lane);
             }
@@ -1319,6 +1165,16 @@ __global__ void __launch_bounds__(512) prefill_tail_logpos_kernel(const PrefillA
     prefill_ring_body<DV, true, 0, false, true>(A);
 }
 
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_tail_fp8_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, 0, true, true>(A);
+}
+
+template <int DV>
+__global__ void __launch_bounds__(512) prefill_tail_fp8_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, 0, true, true>(A);
+}
+
 // The same with the bias made in the kernel.
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_tail_kernel(const PrefillArgs A) {
@@ -1328,6 +1184,16 @@ __global__ void __launch_bounds__(512) prefill_relproj_tail_kernel(const Prefill
 template <int DV, int DR>
 __global__ void __launch_bounds__(512) prefill_relproj_tail_logpos_kernel(const PrefillArgs A) {
     prefill_ring_body<DV, true, DR, false, true>(A);
+}
+
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_tail_fp8_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, false, DR, true, true>(A);
+}
+
+template <int DV, int DR>
+__global__ void __launch_bounds__(512) prefill_relproj_tail_fp8_logpos_kernel(const PrefillArgs A) {
+    prefill_ring_body<DV, true, DR, true, true>(A);
 }
 
 template <int DV>
@@ -2418,15 +2284,14 @@ __global__ void __launch_bounds__(256) rel_rows_kernel(const RelRowsArgs A) {
 namespace {
 
 template <int DV>
-void launch_prefill_fp8_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((prefill_fp8_kernel<DV>), g, blk, 0, s, a);
-}
-
-template <int DV>
 void launch_tail_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_tail_logpos_kernel<DV>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((prefill_tail_kernel<DV>), g, blk, 0, s, a);
+    if (a.kv8) {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_tail_fp8_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_tail_fp8_kernel<DV>), g, blk, 0, s, a);
+    } else {
+        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_tail_logpos_kernel<DV>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((prefill_tail_kernel<DV>), g, blk, 0, s, a);
+    }
 }
 
 template <int DV>
@@ -2443,8 +2308,8 @@ void launch_ring_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
 }  // namespace
 
 // Kernel choice: windowed (every subtile streams bias: the ring kernel) or
-// not (bf16 K/V: whole blocks, then the ring; e4m3 K/V: whole blocks with
-// the bias loaded per lane); per-row logit scale or not.
+// not (whole blocks, then the ring); per-row logit scale or not; bf16 or
+// e4m3 K/V.
 hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     const long long grid = (long long)a.batch * a.n_qt * a.Hkv * a.n_hc;
     if (grid <= 0) return hipSuccess;
@@ -2452,12 +2317,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int dv, hipStream_t s) {
     if (a.W > 0) {
         if (dv == 128) launch_ring_t<128>(a, g, blk, s);
         else launch_ring_t<64>(a, g, blk, s);
-    } else if (!a.kv8) {
+    } else {
         if (dv == 128) launch_tail_t<128>(a, g, blk, s);
         else launch_tail_t<64>(a, g, blk, s);
-    } else {
-        if (dv == 128) launch_prefill_fp8_t<128>(a, g, blk, s);
-        else launch_prefill_fp8_t<64>(a, g, blk, s);
     }
     return hipGetLastError();
 }
@@ -2466,9 +2328,15 @@ namespace {
 
 template <int DV, int DR>
 void launch_relproj_t(const PrefillArgs& a, dim3 g, dim3 blk, hipStream_t s) {
-    if (a.W == 0 && !a.kv8) {  // whole blocks until the first block with bias
-        if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_tail_logpos_kernel<DV, DR>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((prefill_relproj_tail_kernel<DV, DR>), g, blk, 0, s, a);
+    if (a.W == 0) {  // whole blocks until the first block with bias
+        if (a.kv8) {
+            if (a.lscale != nullptr)
+                hipLaunchKernelGGL((prefill_relproj_tail_fp8_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((prefill_relproj_tail_fp8_kernel<DV, DR>), g, blk, 0, s, a);
+        } else {
+            if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_tail_logpos_kernel<DV, DR>), g, blk, 0, s, a);
+            else hipLaunchKernelGGL((prefill_relproj_tail_kernel<DV, DR>), g, blk, 0, s, a);
+        }
     } else if (a.kv8) {
         if (a.lscale != nullptr) hipLaunchKernelGGL((prefill_relproj_fp8_logpos_kernel<DV, DR>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((prefill_relproj_fp8_kernel<DV, DR>), g, blk, 0, s, a);
