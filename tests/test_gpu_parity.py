@@ -64,6 +64,34 @@ def test_prefill_small(case):
     gpu_vs_oracle(b, what=str(case))
 
 
+# Without a window the prefill walks a tile's blocks whole up to the first
+# block in which some row of the tile has bias, and the rest in half blocks
+# through the bias ring. The switch depends on the tile's first position i_lo:
+# the first subtile with bias starts at the multiple of 32 above i_lo - 31 - R.
+# With R = 256 and one 64-row tile per sequence (G = 4), the contexts below
+# put it at the first block (100, 286, 287), at each 32-key offset inside a
+# block (383, 415, 447, 479) and after one, two or three whole blocks (383,
+# 511, 543, 639: odd and even counts, which use the two whole-block buffers
+# in the other order), and late in a long context (1200, 3001). R = 1 leaves
+# bias on the diagonal subtiles only; R = 2000 puts it on every block.
+TAIL_SWITCH = [
+    # q_lens, ctx_lens, dv, R
+    ([64] * 12, [100, 286, 287, 383, 415, 447, 479, 511, 543, 639, 1200, 3001], 128, 256),
+    ([200, 130], [0, 1000], 128, 256),
+    ([64, 150], [700, 2000], 64, 1),
+    ([100, 64], [300, 1500], 64, 2000),
+]
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "e4m3"])
+@pytest.mark.parametrize("case", TAIL_SWITCH, ids=lambda c: f"dv{c[2]}R{c[3]}_{len(c[0])}seq")
+def test_prefill_whole_blocks_then_ring(case, kv_fp8):
+    q_lens, ctx, dv, R = case
+    say(f"prefill whole blocks then ring {case} e4m3={kv_fp8}")
+    b = W.make_prefill(12, q_lens, ctx, 8, 2, dv, R, 0, kv_fp8=kv_fp8)
+    gpu_vs_oracle(b, what=f"{case} e4m3={kv_fp8}")
+
+
 def test_tiny_prefill_workload():
     say("tiny_prefill_256")
     gpu_vs_oracle(W.build("tiny_prefill_256"), what="tiny")
