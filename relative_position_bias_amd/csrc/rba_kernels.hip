@@ -649,36 +649,36 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
 }
 
 // ---------------------------------------------------------------------------
-// Prefill with the bias produced in the kernel (rel = r @ rel_logits_proj)
+// Prefill: the bias through a per-column band ring
 //
-// Instead of reading rel [rows, Hq, R] from HBM, each wave computes the bias
-// its 32 columns need from r (d_r = 32, 64 or 128 values per column, held as
-// an MFMA operand) and the projection (rows of d_r values per distance, read
-// from L2). The wave's columns are 32 consecutive positions w_lo + n of one
-// head, so for the 32 keys js .. js + 31 of a subtile column n needs the
-// distances (w_lo - js) + n - 31 .. (w_lo - js) + n: 63 distinct distances
-// across the wave, sheared by n. Per subtile the wave computes a band
-// T(js)[rho, n] = r_n . proj[(w_lo - js) - 32 + rho] for rho = 0..31 with
-// d_r / 16 32x32x16 MFMAs and stores it into a per-column ring of 64 distances that
-// also holds T(js - 32) (the distances (w_lo - js) .. + 31). The shear is
-// undone on the way out: each lane reads its 16 bias values as two runs of 8
-// consecutive ring entries starting at a lane-dependent slot. Ring slot of
-// distance d at subtile js: (d - (w_lo - js) + 32 + 32 par(js)) mod 64,
-// par(js) = (js / 32) mod 2; T(js) occupies slots 32 par .. 32 par + 31; slots
-// 0..7 are duplicated at 64..71 so that no run wraps.
+// A wave's 32 columns are 32 consecutive positions w_lo + n of one head, so
+// for the 32 keys js .. js + 31 of a subtile column n needs the distances
+// (w_lo - js) + n - 31 .. (w_lo - js) + n: 63 distinct distances across the
+// wave, sheared by n. Per subtile the wave puts a band T(js)[rho, n], the
+// bias of column n at distance (w_lo - js) - 32 + rho for rho = 0..31, into a
+// per-column ring of 64 distances that also holds T(js - 32) (the distances
+// (w_lo - js) .. + 31). The shear is undone on the way out: each lane reads
+// its 16 bias values as two runs of 8 consecutive ring entries starting at a
+// lane-dependent slot. Ring slot of distance d at subtile js:
+// (d - (w_lo - js) + 32 + 32 par(js)) mod 64, par(js) = (js / 32) mod 2;
+// T(js) occupies slots 32 par .. 32 par + 31; slots 0..7 are duplicated at
+// 64..71 so that no run wraps.
+//
+// Two band sources. Over a materialised rel (DR = 0) the band is rel entries
+// that start at the same distance in every column's row: eight lanes load
+// one row's 128 bytes, so one load instruction covers 8 rows (loading each
+// lane's own 8-distance runs straight from HBM instead spreads every
+// instruction over 32 rows, and where every subtile streams bias the vector
+// memory path then saturates on the number of rows in flight). With the bias
+// made in the kernel (rel = r @ rel_logits_proj, "Attention with a relative
+// bias"; DR = 32, 64 or 128) the wave computes T(js)[rho, n] =
+// r_n . proj[(w_lo - js) - 32 + rho] with DR / 16 32x32x16 MFMAs, r_n held
+// as an MFMA operand for the whole sweep and the projection rows read from
+// L2.
 //
 // The ring (32 x 76 floats per wave, 76 KiB for 8 waves) does not fit beside
 // double-buffered whole K/V blocks, so K/V move in half blocks of 64 keys
-// (two subtiles per barrier).
-//
-// The prefill over a materialised rel uses the same ring (DR = 0): band
-// T(jb) is then the rel entries of the 32 distances (w_lo - jb) - 32 ..
-// (w_lo - jb) - 1 of each column's row, which start at the same distance in
-// every row. Eight lanes load one row's 128 bytes, so one load instruction
-// covers 8 rows; loading each lane's own 8-distance runs straight from HBM
-// instead spreads every instruction over 32 rows, and where every subtile
-// streams bias the vector memory path then saturates on the number of rows
-// in flight.
+// (two subtiles per barrier) wherever bias is in use.
 // ---------------------------------------------------------------------------
 constexpr int RSTRIDE = 76;  // floats per column in the band ring (64 + 8 duplicated + 4 pad)
 
@@ -703,8 +703,9 @@ struct BandSrc<0> {
 // output.
 //
 // WB (no window): the blocks before the first subtile that carries bias for
-// any row of the tile are walked whole (128-key blocks, no bias code); the ring and the half-block stages take over from the
-// first block with bias. One LDS area is laid out twice. bf16 K/V: two
+// any row of the tile are walked whole (128-key blocks, no bias code); the
+// ring and the half-block stages take over from the first block with bias.
+// One LDS area is laid out twice. bf16 K/V: two
 // whole-block buffers, between which the whole blocks alternate so that the
 // last one is in buffer 1; the ring phase then puts its stages in buffer 0
 // and the rings in buffer 1 and the LDS after it. e4m3 K/V: one bf16
@@ -786,9 +787,9 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     const int s_lo = (A.W > 0 ? max(0, i_lo - A.W + 1) : 0) / HB;
     const int s_hi = i_hi / HB;
     const int kb_lo = s_lo / SPB, kb_hi = s_hi / SPB;
-    // WB: whole blocks kb_lo .. kb_sw - 1, then stages from s_first. A
-    // subtile js carries bias for the tile's first row i_lo (and so for no
-    // row at all before it) iff i_lo - (js + 31) < R.
+    // WB: whole blocks kb_lo .. kb_sw - 1, then stages from s_first. Subtile
+    // js carries bias for some row of the tile iff it does for the tile's
+    // first row i_lo (the others lie further from it): iff i_lo - (js + 31) < R.
     int kb_sw = kb_lo;
     if constexpr (WB) {
         const int t = i_lo - 31 - A.R;
@@ -847,9 +848,9 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
     };
 
     // The start issues every independent load at once (q, r, the first two
-    // bands' projection rows, the block-table slice) behind a single wait,
-    // then the first copy, then the first two bands; so one HBM round trip
-    // precedes the copy instead of a chain of them.
+    // bands' sources, the block-table slice) behind a single wait, then the
+    // first copy, then the first two bands; so one HBM round trip precedes
+    // the copy instead of a chain of them.
     bf16x8 rreg[DR > 0 ? DR / 16 : 1];  // r of the lane's column: the band's B operand
     BandSrc<DR> pv;                      // sources of the next band
     BandSrc<DR> pv0;                     // (start only) sources of the band before the first
@@ -1000,7 +1001,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         }
     }
     int band_js = INT_MIN;  // last band in the ring
-    int pv_js = INT_MIN;    // band whose projection rows pv holds
+    int pv_js = INT_MIN;    // band whose sources pv holds
 
     // WB: the whole blocks (no row of the tile has bias there). The last one
     // starts the ring phase's first copy into the other buffer; the first two
@@ -1059,9 +1060,9 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         band_js = js_lo;
     }
 
-    // One stage (two subtiles). Each band's projection rows are requested one
-    // subtile ahead; the next stage's first band's at the end of the stage,
-    // so they have landed by its barrier.
+    // One stage (two subtiles). Each band's sources are requested one subtile
+    // ahead; the next stage's first band's at the end of the stage, so they
+    // have landed by its barrier.
     auto step = [&](const __bf16* Kc, const __bf16* Vc, __bf16* Kn, __bf16* Vn, int s) {
         vm_wait_all();
         lds_barrier();
