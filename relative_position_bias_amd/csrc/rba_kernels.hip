@@ -331,6 +331,26 @@ __device__ __forceinline__ void sm_probs(Cols<DV>& C, const float (&x)[16], bf16
     }
 }
 
+// p = exp2(x) and the bf16 B operands of P.V, without touching the row sum;
+// returns the sum of the lane's 16 probabilities.
+__device__ __forceinline__ float sm_probs_sum(const float (&x)[16], bf16x8 (&pb)[2]) {
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = __builtin_amdgcn_exp2f(x[8 * c + i]);
+            sum += p;
+            pb[c][i] = (__bf16)p;
+        }
+    }
+    return sum;
+}
+
+// A lane whose 16 probabilities sum to at most this has none above 2^TAU
+// (the sum is at least its largest term, up to fp32 rounding of 16 terms).
+constexpr float PSUM_TRIGGER = 65536.f * 0.999f;
+
 template <int DV>
 __device__ __forceinline__ bool need_mask_of(const Cols<DV>& C, int js, int W) {
     return C.phantom || (js + 31 > C.w_lo) || (W > 0 && C.w_hi - js >= W);
@@ -620,11 +640,19 @@ __device__ __forceinline__ float rel_bias(const RelVals& rv, int r, int pos, int
     return d < R ? rv.v[r] : 0.f;
 }
 
-// sm_scores with the bias taken from registers.
+// The column's max over both lane halves.
+__device__ __forceinline__ float sm_colmax(const float (&x)[16]) {
+    float M = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
+    return halves_max(M);
+}
+
+// The logits of sm_scores with the bias taken from registers (no max).
 template <int DV>
-__device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s, bool has_bias, const RelVals& rv,
-                                              bool inside, bool need_mask, int js, int W, int R, float c1, float l2e,
-                                              int lane, float (&x)[16]) {
+__device__ __forceinline__ void sm_logits_rv(const Cols<DV>& C, const f32x16& s, bool has_bias, const RelVals& rv,
+                                             bool inside, bool need_mask, int js, int W, int R, float c1, float l2e,
+                                             int lane, float (&x)[16]) {
     if (has_bias) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -642,10 +670,15 @@ __device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s
             x[r] = vis ? x[r] : -INFINITY;
         }
     }
-    float M = x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) M = fmaxf(M, x[r]);
-    return halves_max(M);
+}
+
+// sm_scores with the bias taken from registers.
+template <int DV>
+__device__ __forceinline__ float sm_scores_rv(const Cols<DV>& C, const f32x16& s, bool has_bias, const RelVals& rv,
+                                              bool inside, bool need_mask, int js, int W, int R, float c1, float l2e,
+                                              int lane, float (&x)[16]) {
+    sm_logits_rv(C, s, has_bias, rv, inside, need_mask, js, W, R, c1, l2e, lane, x);
+    return sm_colmax(x);
 }
 
 // ---------------------------------------------------------------------------
@@ -951,13 +984,35 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         RelVals rb;
         if (biased) read_bias(js, rb);
         float x[16];
-        float M = sm_scores_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, c1f, l2f, lane, x);
-        if (__any(!C.m_set || sm_trigger(C, M))) {
-            if (__any(!C.m_set)) sm_init_ref(C, M, x);
-            if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
-        }
+        sm_logits_rv(C, sc, biased, rb, true, need_mask_of(C, js, A.W), js, A.W, A.R, c1f, l2f, lane, x);
         bf16x8 pb[2];
-        sm_probs(C, x, pb);
+        float psum;
+        if constexpr (WB) {
+            // No window: the probabilities against the current reference
+            // first. The column max is needed only where a column has no
+            // reference yet or some lane's sum says a probability may exceed
+            // 2^TAU; the lazy-rescale decision is then the usual one (taken on
+            // the max), so the results do not depend on this shortcut. (With a
+            // window the first subtiles of a sweep reach the columns at
+            // different keys, and computing the max up front measured faster.)
+            psum = sm_probs_sum(x, pb);
+            if (__any(!C.m_set || psum > PSUM_TRIGGER)) {
+                float M = sm_colmax(x);
+                if (__any(!C.m_set || sm_trigger(C, M))) {
+                    if (__any(!C.m_set)) sm_init_ref(C, M, x);
+                    if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+                    psum = sm_probs_sum(x, pb);
+                }
+            }
+        } else {
+            float M = sm_colmax(x);
+            if (__any(!C.m_set || sm_trigger(C, M))) {
+                if (__any(!C.m_set)) sm_init_ref(C, M, x);
+                if (__any(sm_trigger(C, M))) sm_rescale(C, M, x);
+            }
+            psum = sm_probs_sum(x, pb);
+        }
+        C.l_sum += psum;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
