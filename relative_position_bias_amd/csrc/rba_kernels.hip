@@ -516,13 +516,11 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds) {
 }
 
 // The copies are issued by the first NW waves (NW = 8 or 4), 32 / NW K and
-// 2 DV / (8 NW) V instructions each. Waves w and w + 4 share a SIMD and the
-// lower one is served first, so it reaches the block barrier early; with
-// NW = 4 the early waves issue all copies there, which balances the pair when
-// the score/softmax chain dominates (no window). With a window every subtile
-// also streams its bias from HBM and spreading the copies over all 8 waves
-// is better. ROWS (128 or 64) rows are copied, from kblk / vblk on: a whole
-// block or half of one, in the same per-row layout.
+// 2 DV / (8 NW) V instructions each (for ROWS = 128). Waves w and w + 4 share
+// a SIMD and the lower one is served first, so it reaches the barrier early;
+// with NW = 4 the early waves issue all copies there, which balances the
+// pair. ROWS (128 or 64) rows are copied, from kblk / vblk on: a whole block
+// or half of one, in the same per-row layout.
 template <int DV, int NW, int ROWS = BS>
 __device__ __forceinline__ void kv_dma(__bf16* Ks, __bf16* Vs, const uint16_t* kblk, const uint16_t* vblk,
                                        int nvalid, int wid, int lane) {
@@ -747,7 +745,7 @@ struct BandSrc<0> {
 // above them, the others after the staging area.
 template <int DV, bool LS, int DR, bool KV8 = false, bool WB = false>
 __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
-    constexpr int NW = 8;   // every wave issues stage copies
+    constexpr int NW = WB ? 8 : 4;  // waves that issue the stage copies (measured per kernel)
     constexpr int HB = 64;  // keys per K/V stage (half a block)
     constexpr int SPB = BS / HB;
     constexpr int RING_W = 32 * RSTRIDE;        // floats of one wave's ring
