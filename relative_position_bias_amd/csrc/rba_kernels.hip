@@ -893,15 +893,20 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         load_p(pv, js_lo);
     }
     load_q(C, A.q + trow * DQK, lane);
+    auto load_r = [&]() {
 #pragma unroll
-    for (int st = 0; st < DR / 16; ++st) {
-        if (real) {
-            rreg[st] = *reinterpret_cast<const bf16x8*>(A.r + trow * DR + 16 * st + 8 * hh);
-        } else {
+        for (int st = 0; st < DR / 16; ++st) {
+            if (real) {
+                rreg[st] = *reinterpret_cast<const bf16x8*>(A.r + trow * DR + 16 * st + 8 * hh);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) rreg[st][i] = (__bf16)0.f;
+                for (int i = 0; i < 8; ++i) rreg[st][i] = (__bf16)0.f;
+            }
         }
-    }
+    };
+    // WB with whole blocks first: r is loaded after them, so that it is not
+    // held through the blocks that need no bias.
+    if (!WB || n1 == 0) load_r();
     init_acc(C);
     // A device length that breaks the caller's contract (fewer keys than new
     // rows, or more keys than the block-table row can address) makes the
@@ -1098,6 +1103,7 @@ __device__ __forceinline__ void prefill_ring_body(const PrefillArgs A) {
         if (n1 > 0 && ring_phase) {
             // (requested only now, so that they are not live across the last
             // whole block's compute)
+            load_r();
             if (rel_active(js_lo)) {
                 load_p(pv0, js_lo - 32);
                 load_p(pv, js_lo);
