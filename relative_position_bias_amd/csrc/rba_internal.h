@@ -29,7 +29,7 @@ struct PrefillArgs {
     int32_t num_blocks, max_blocks, batch;
     int32_t Hq, Hkv, G, R, W;
     float c1;                 // scale * log2(e), times the K dequantization scale for e4m3 K/V
-    int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3 (prefill_kernel only)
+    int32_t kv8;              // K/V cache elements: 0 = bf16, 1 = e4m3
     float v_scale;            // V dequantization scale (1 for bf16 K/V)
     int32_t hpw;              // query heads per workgroup (divides G)
     int32_t QT;               // query rows per tile = 32 * (8 / hpw)
