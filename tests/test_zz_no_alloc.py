@@ -32,10 +32,13 @@ CALLS = [
      (62, 2, 1, 32, 8, 128, 1024, 0, [700, 1500], 3)),
     ((63, 2, 4, 64, 8, 64, 1024, 0, [30000, 5000], 0),
      (64, 1, 4, 64, 8, 64, 512, 300, [2000], 0)),
+    # 48 columns (both column groups in one workgroup)
+    ((66, 2, 8, 48, 8, 128, 1024, 0, [12000, 3000], 0),
+     (67, 1, 8, 48, 8, 128, 1024, 0, [2500], 2)),
 ]
 
 
-@pytest.mark.parametrize("pair", CALLS, ids=["16col", "32col"])
+@pytest.mark.parametrize("pair", CALLS, ids=["16col", "32col", "48col"])
 def test_noalloc_decode_equals_workspace_decode(pair):
     for seed, batch, n_q, Hq, Hkv, dv, R, Wn, lens, splits in pair:
         say(f"no-alloc decode seed={seed} lens={lens} splits={splits}")
