@@ -189,11 +189,11 @@ def bf16_p_bound(batch: workloads.Batch, rows=None, slack=1e-5):
     """Per-element bound on |o1 - o2| for two GPU results of the same call
     that differ only in the reference against which P is rounded to bf16
     (another split count, another block order). Each result is
-    sum_j p~_j v_j / sum_j p_j with |p~_j - p_j| <= 2^-9 p_j (round to nearest
-    even, 8 significant bits), so it lies within 2^-9 * E_p|v| of the exact
-    value, E_p|v| being the softmax-weighted mean of |v|: the oracle run on
-    |V|. Two results differ by at most 2^-8 * E_p|v|, plus fp32 rounding
-    (`slack`). bf16 caches only."""
+    sum_j p~_j v_j / sum_j p_j with |p~_j - p_j| <= 2^-8 p_j (round to nearest
+    even with 8 significant bits: the unit roundoff is 2^-8), so it lies
+    within 2^-8 * E_p|v| of the exact value, E_p|v| being the softmax-weighted
+    mean of |v|: the oracle run on |V|. Two results differ by at most
+    2^-7 * E_p|v|, plus fp32 rounding (`slack`). bf16 caches only."""
     babs = workloads.Batch(**{**batch.__dict__, "v_cache": batch.v_cache.abs()})
     ev, _ = oracle_batch(babs, rows)
-    return 2.0 ** -8 * ev + slack
+    return 2.0 ** -7 * ev + slack

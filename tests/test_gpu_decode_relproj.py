@@ -79,7 +79,7 @@ def test_decode_relproj_equals_decode_on_the_oracle_bias(case):
     fp32. The producer's fp32 sums differ from that by a few ulps of the bias;
     where such a difference moves a probability across a bf16 rounding
     boundary, the output moves by at most that probability's rounding. So
-    the outputs must agree element by element within the bf16-P bound (2^-8
+    the outputs must agree element by element within the bf16-P bound (2^-7
     of the softmax-weighted mean |v|, plus fp32 slack), and the lse, which
     sums the fp32 probabilities, to 1e-5."""
     batch, n_q, lens, Hq, Hkv, dv, R, Wn, d_r, ph = case
